@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs for the GRINQH decode-stage vector-matrix multiply.
+
+This module only *draws* inputs: weight matrices already quantised to 8-bit
+asymmetric codes with per-(128-row group, column) fp16 scale and zero, fp16
+activation vectors, and the precision distributions P that the workloads use.
+It holds none of the GRINQH method's arithmetic (no threshold calibration, no
+precision assignment, no bit planes, no reconstruction).  Both the fp64 oracle
+and the HIP library consume what it returns; neither is imported here.
+
+Recipe (the pages measure on trained Llama-3 / Qwen3 weights and on text
+datasets that are not available; these seeded draws stand in for them, keeping
+only the model shapes):
+
+* Weights ``W ~ N(0, 0.02^2)`` in fp32, quantised round-to-nearest at 8 bits,
+  one (scale, zero) pair per group of 128 input rows and per output column, as
+  in the RTN base the paper builds on ("Models and Baselines", section 4, group
+  size G = 128).  ``s = (max - min) / 255`` and ``z = min`` are rounded
+  round-to-nearest-even to fp16, and codes use those rounded values:
+  ``q = clip(rint((w - z) / s), 0, 255)`` (``q = 0`` where ``s == 0``).
+  The base quantiser is an input recipe: the paper treats the quantisation
+  step as independent of GRINQH (Appendix D.1).
+* Activations: ``|x_i| = exp(N(0, 1))`` with a random sign; a fixed set of
+  ``ceil(0.01 K)`` outlier input channels per matrix is scaled by 20 in every
+  vector drawn for that matrix (persistent outlier channels, section 3.1's
+  motivation).  Cast to fp16.
+* Seeds: ``numpy.random.SeedSequence([config, matrix, role])`` with role 0 for
+  W, 1 for the outlier channel set, 2 for calibration vectors, 3 for test
+  vectors.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+GROUP = 128          # rows per (scale, zero) group
+N_CALIB = 64         # calibration vectors per matrix
+WEIGHT_STD = 0.02
+OUTLIER_FRACTION = 0.01
+OUTLIER_SCALE = 20.0
+
+ROLE_W, ROLE_OUTLIERS, ROLE_CALIB, ROLE_TEST = 0, 1, 2, 3
+
+# Precision level sets and target distributions P = (p_0, ..., p_n).  Every P
+# below sums to 1 and its weighted average bit width is the key of the entry.
+LEVELS_5 = (0, 2, 3, 4, 8)
+LEVELS_4 = (0, 2, 4, 8)
+
+P_LEVELS_5 = {
+    2: (0.35, 0.30, 0.20, 0.10, 0.05),
+    3: (0.25, 0.20, 0.20, 0.20, 0.15),
+    4: (0.15, 0.10, 0.20, 0.30, 0.25),
+    8: (0.0, 0.0, 0.0, 0.0, 1.0),
+}
+# The tiny workload's thresholds are the 25/50/75/90 % quantiles of |x|.
+P_TINY = (0.25, 0.25, 0.25, 0.15, 0.10)
+
+P_LEVELS_4 = {
+    0.5: (0.88, 0.05, 0.04, 0.03),
+    1: (0.75, 0.10, 0.10, 0.05),
+    2: (0.50, 0.20, 0.20, 0.10),
+    3: (0.30, 0.20, 0.35, 0.15),
+    4: (0.15, 0.20, 0.40, 0.25),
+    6: (0.10, 0.10, 0.15, 0.65),
+    8: (0.0, 0.0, 0.0, 1.0),
+}
+
+# Workload shapes (K input rows x N output columns).
+LLAMA3_8B_LAYER = {
+    "q": (4096, 4096), "k": (4096, 1024), "v": (4096, 1024), "o": (4096, 4096),
+    "gate": (4096, 14336), "up": (4096, 14336), "down": (14336, 4096),
+}
+QWEN3_8B_LAYER = {
+    "q": (4096, 4096), "k": (4096, 1024), "v": (4096, 1024), "o": (4096, 4096),
+    "gate": (4096, 12288), "up": (4096, 12288), "down": (12288, 4096),
+}
+QWEN3_8B_LAYERS = 36
+LLAMA3_70B_MLP = {"gate": (8192, 28672), "down": (28672, 8192)}
+
+
+def rng(config: int, matrix: int, role: int) -> np.random.Generator:
+    """Independent PCG64 stream for one (config, matrix, role) triple."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([config, matrix, role])))
+
+
+def n_groups(K: int) -> int:
+    return (K + GROUP - 1) // GROUP
+
+
+def rtn_quantize(w: np.ndarray):
+    """Round-to-nearest 8-bit asymmetric quantisation of fp32 ``w[K][N]``.
+
+    Returns ``(codes u8[K][N], scales f16[G][N], zeros f16[G][N])``.  The last
+    group may hold fewer than 128 rows.
+    """
+    K, N = w.shape
+    G = n_groups(K)
+    codes = np.empty((K, N), dtype=np.uint8)
+    scales = np.empty((G, N), dtype=np.float16)
+    zeros = np.empty((G, N), dtype=np.float16)
+    for g in range(G):
+        blk = w[g * GROUP:(g + 1) * GROUP].astype(np.float64)
+        lo = blk.min(axis=0)
+        hi = blk.max(axis=0)
+        s16 = ((hi - lo) / 255.0).astype(np.float16)
+        z16 = lo.astype(np.float16)
+        s64 = s16.astype(np.float64)
+        z64 = z16.astype(np.float64)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.rint((blk - z64) / s64)
+        q = np.where(s64 == 0.0, 0.0, q)
+        codes[g * GROUP:(g + 1) * GROUP] = np.clip(q, 0, 255).astype(np.uint8)
+        scales[g] = s16
+        zeros[g] = z16
+    return codes, scales, zeros
+
+
+def make_weights(K: int, N: int, config: int = 0, matrix: int = 0):
+    """Seeded ``W ~ N(0, 0.02^2)`` quantised by :func:`rtn_quantize`."""
+    r = rng(config, matrix, ROLE_W)
+    codes = np.empty((K, N), dtype=np.uint8)
+    G = n_groups(K)
+    scales = np.empty((G, N), dtype=np.float16)
+    zeros = np.empty((G, N), dtype=np.float16)
+    # Draw and quantise one group at a time so large matrices stay small in memory.
+    for g in range(G):
+        rows = min(GROUP, K - g * GROUP)
+        w = r.standard_normal((rows, N), dtype=np.float32) * np.float32(WEIGHT_STD)
+        c, s, z = rtn_quantize(w)
+        codes[g * GROUP:g * GROUP + rows] = c
+        scales[g] = s[0]
+        zeros[g] = z[0]
+    return codes, scales, zeros
+
+
+def outlier_rows(K: int, config: int = 0, matrix: int = 0) -> np.ndarray:
+    """Fixed per-matrix set of ceil(1% K) outlier input channels (sorted)."""
+    n_out = int(math.ceil(OUTLIER_FRACTION * K))
+    r = rng(config, matrix, ROLE_OUTLIERS)
+    return np.sort(r.choice(K, size=n_out, replace=False))
+
+
+def make_activations(K: int, count: int, config: int = 0, matrix: int = 0,
+                     role: int = ROLE_TEST) -> np.ndarray:
+    """``count`` fp16 activation vectors of length K, shape [count][K]."""
+    r = rng(config, matrix, role)
+    mag = np.exp(r.standard_normal((count, K)))
+    sign = np.where(r.random((count, K)) < 0.5, -1.0, 1.0)
+    x = mag * sign
+    x[:, outlier_rows(K, config, matrix)] *= OUTLIER_SCALE
+    return x.astype(np.float16)
+
+
+def make_calibration(K: int, config: int = 0, matrix: int = 0, count: int = N_CALIB) -> np.ndarray:
+    return make_activations(K, count, config, matrix, ROLE_CALIB)
+
+
+@dataclass
+class Layer:
+    """One linear layer's synthetic inputs."""
+    K: int
+    N: int
+    codes: np.ndarray      # u8 [K][N]
+    scales: np.ndarray     # f16 [G][N]
+    zeros: np.ndarray      # f16 [G][N]
+    calib: np.ndarray      # f16 [N_CALIB][K]
+    x: np.ndarray          # f16 [n_test][K]
+
+
+def make_layer(K: int, N: int, config: int = 0, matrix: int = 0, n_test: int = 1,
+               n_calib: int = N_CALIB) -> Layer:
+    codes, scales, zeros = make_weights(K, N, config, matrix)
+    calib = make_calibration(K, config, matrix, n_calib)
+    x = make_activations(K, n_test, config, matrix, ROLE_TEST)
+    return Layer(K, N, codes, scales, zeros, calib, x)

@@ -1,0 +1,57 @@
+"""Checks of the seeded input generator (shapes, determinism, RTN bounds)."""
+import math
+
+import numpy as np
+import pytest
+
+import synthetic
+
+
+def test_deterministic_and_role_separated():
+    a = synthetic.make_layer(256, 64, config=0, matrix=0)
+    b = synthetic.make_layer(256, 64, config=0, matrix=0)
+    for f in ("codes", "scales", "zeros", "calib", "x"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+    c = synthetic.make_layer(256, 64, config=0, matrix=1)
+    assert not np.array_equal(a.codes, c.codes)
+    assert not np.array_equal(a.calib[0], a.x[0])
+
+
+def test_shapes_and_dtypes():
+    lay = synthetic.make_layer(300, 70, config=0, matrix=0, n_test=3)
+    assert lay.codes.shape == (300, 70) and lay.codes.dtype == np.uint8
+    assert lay.scales.shape == (3, 70) and lay.scales.dtype == np.float16
+    assert lay.zeros.shape == (3, 70)
+    assert lay.calib.shape == (64, 300) and lay.calib.dtype == np.float16
+    assert lay.x.shape == (3, 300)
+
+
+def test_rtn_round_to_nearest_bound():
+    r = np.random.default_rng(0)
+    w = (r.standard_normal((300, 40)) * 0.02).astype(np.float32)
+    q, s, z = synthetic.rtn_quantize(w)
+    g = np.arange(300) // 128
+    s64 = s[g].astype(np.float64)
+    z64 = z[g].astype(np.float64)
+    w_hat = s64 * q + z64
+    inside = (q > 0) & (q < 255)
+    assert np.all(np.abs(w_hat - w)[inside] <= s64[inside] * 0.5 * (1 + 1e-9))
+    assert inside.mean() > 0.95
+    assert q.min() == 0 and q.max() == 255
+
+
+def test_outlier_channels():
+    K = 4096
+    x = synthetic.make_activations(K, 16, config=1, matrix=0).astype(np.float64)
+    rows = synthetic.outlier_rows(K, config=1, matrix=0)
+    assert len(rows) == math.ceil(0.01 * K)
+    ratio = np.median(np.abs(x[:, rows])) / np.median(np.abs(np.delete(x, rows, axis=1)))
+    assert 15 < ratio < 27
+
+
+@pytest.mark.parametrize("table,levels", [(synthetic.P_LEVELS_5, synthetic.LEVELS_5),
+                                          (synthetic.P_LEVELS_4, synthetic.LEVELS_4)])
+def test_precision_tables(table, levels):
+    for avg, P in table.items():
+        assert sum(P) == pytest.approx(1.0, abs=1e-12)
+        assert sum(p * b for p, b in zip(P, levels)) == pytest.approx(avg, abs=1e-12)
