@@ -1,0 +1,163 @@
+// C-ABI entry points: host-side validation, then one launcher per call.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.hpp"
+
+namespace grinqh {
+
+static thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GRINQH_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+  return GRINQH_OK;
+}
+
+static inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+static int check_assign_params(const float* thresholds, const uint8_t* levels, int n, AssignParams* ap) {
+  if (n < 0 || n > kMaxThresholds) return fail(GRINQH_EINVAL, "n = %d thresholds, expected 0..%d", n, kMaxThresholds);
+  if (n > 0 && !thresholds) return fail(GRINQH_EINVAL, "thresholds is NULL");
+  if (!levels) return fail(GRINQH_EINVAL, "levels is NULL");
+  memset(ap, 0, sizeof(*ap));
+  ap->n = n;
+  for (int t = 0; t < n; ++t) {
+    const float v = thresholds[t];
+    if (isnan(v) || v < 0.0f) return fail(GRINQH_EINVAL, "threshold %d is %g (must be >= 0, not NaN)", t, (double)v);
+    if (t > 0 && v < thresholds[t - 1]) return fail(GRINQH_EINVAL, "thresholds decrease at index %d", t);
+    ap->th[t] = v;
+  }
+  for (int t = 0; t <= n; ++t) {
+    if (levels[t] > GRINQH_MAX_BITS) return fail(GRINQH_EINVAL, "level %d is %u (must be 0..8)", t, (unsigned)levels[t]);
+    ap->lv[t] = levels[t];
+  }
+  return GRINQH_OK;
+}
+
+static int check_vmm_common(const void* planes, const void* scales, const void* zeros, const void* x,
+                            const void* y, int64_t K, int64_t N, const void* ws, size_t ws_bytes) {
+  if (!planes || !scales || !zeros || !x || !y) return fail(GRINQH_EINVAL, "NULL data pointer");
+  if (K <= 0 || N <= 0) return fail(GRINQH_EINVAL, "K = %lld, N = %lld must be positive", (long long)K, (long long)N);
+  if (K >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "K or N too large");
+  if (K * padded_cols(N) >= (int64_t(1) << 40)) return fail(GRINQH_EINVAL, "store larger than 2^40 bytes");
+  const VmmGeometry g = vmm_geometry(K, N);
+  if (!ws && g.bytes > 0) return fail(GRINQH_EINVAL, "workspace is NULL");
+  if ((int64_t)ws_bytes < g.bytes)
+    return fail(GRINQH_EINVAL, "workspace has %zu bytes, needs %lld", ws_bytes, (long long)g.bytes);
+  return GRINQH_OK;
+}
+
+}  // namespace grinqh
+
+using namespace grinqh;
+
+extern "C" {
+
+int grinqh_layout_version(void) { return 2; }
+
+const char* grinqh_status_string(int status) {
+  switch (status) {
+    case GRINQH_OK: return "ok";
+    case GRINQH_EINVAL: return "invalid argument";
+    case GRINQH_EDEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* grinqh_last_error(void) { return g_last_error; }
+
+int64_t grinqh_planes_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0) return -1;
+  return K * padded_cols(N);
+}
+
+int64_t grinqh_workspace_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0) return -1;
+  return vmm_geometry(K, N).bytes;
+}
+
+int grinqh_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (!workspace && workspace_bytes) return fail(GRINQH_EINVAL, "workspace is NULL");
+  if (workspace_bytes == 0) return GRINQH_OK;
+  return launch_fill_zero(workspace, workspace_bytes, as_stream(stream));
+}
+
+int grinqh_pack(const uint8_t* codes, int64_t K, int64_t N, uint8_t* planes, void* stream) {
+  g_last_error[0] = 0;
+  if (!codes || !planes) return fail(GRINQH_EINVAL, "NULL pointer");
+  if (K <= 0 || N <= 0) return fail(GRINQH_EINVAL, "K = %lld, N = %lld must be positive", (long long)K, (long long)N);
+  if (K >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "K or N too large");
+  if (K * padded_cols(N) >= (int64_t(1) << 40)) return fail(GRINQH_EINVAL, "store larger than 2^40 bytes");
+  return launch_pack(codes, K, N, planes, as_stream(stream));
+}
+
+int grinqh_calibrate(const uint16_t* calib, int64_t V, int64_t K, const double* P, int n_levels,
+                     float* thresholds, void* stream) {
+  g_last_error[0] = 0;
+  if (!calib || !P || (!thresholds && n_levels > 1)) return fail(GRINQH_EINVAL, "NULL pointer");
+  if (V <= 0 || K <= 0) return fail(GRINQH_EINVAL, "V = %lld, K = %lld must be positive", (long long)V, (long long)K);
+  if (V >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "V or K too large");
+  if (n_levels < 1 || n_levels > kMaxThresholds + 1) return fail(GRINQH_EINVAL, "n_levels = %d, expected 1..9", n_levels);
+  double cuts[kMaxThresholds];
+  double acc = 0.0;
+  for (int k = 0; k < n_levels; ++k) {
+    if (!isfinite(P[k]) || P[k] < 0.0) return fail(GRINQH_EINVAL, "P[%d] = %g must be finite and >= 0", k, P[k]);
+  }
+  // c_k = p_0 + ... + p_{k-1}, accumulated left to right.
+  for (int k = 1; k < n_levels; ++k) {
+    acc = acc + P[k - 1];
+    cuts[k - 1] = acc;
+  }
+  if (n_levels == 1) return GRINQH_OK;
+  return launch_calibrate(calib, V, K, cuts, n_levels - 1, thresholds, as_stream(stream));
+}
+
+int grinqh_assign_bits(const uint16_t* x, int64_t K, const float* thresholds, const uint8_t* levels,
+                       int n, uint8_t* bits, int32_t* active_idx, int32_t* n_active, void* stream) {
+  g_last_error[0] = 0;
+  if (!x || !bits || !active_idx || !n_active) return fail(GRINQH_EINVAL, "NULL pointer");
+  if (K <= 0 || K >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "K = %lld out of range", (long long)K);
+  AssignParams ap;
+  int st = check_assign_params(thresholds, levels, n, &ap);
+  if (st != GRINQH_OK) return st;
+  return launch_assign(x, K, ap, bits, active_idx, n_active, as_stream(stream));
+}
+
+int grinqh_vmm(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+               const uint16_t* x, const uint8_t* bits, const int32_t* active_idx,
+               const int32_t* n_active, int64_t K, int64_t N, float* y,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_vmm_common(planes, scales, zeros, x, y, K, N, workspace, workspace_bytes);
+  if (st != GRINQH_OK) return st;
+  if (!bits || !active_idx || !n_active) return fail(GRINQH_EINVAL, "NULL assignment pointer");
+  return launch_vmm_list(planes, scales, zeros, x, bits, active_idx, n_active, K, N, y, workspace,
+                         as_stream(stream));
+}
+
+int grinqh_decode_vmm(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                      const uint16_t* x, int64_t K, int64_t N,
+                      const float* thresholds, const uint8_t* levels, int n, float* y,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_vmm_common(planes, scales, zeros, x, y, K, N, workspace, workspace_bytes);
+  if (st != GRINQH_OK) return st;
+  AssignParams ap;
+  st = check_assign_params(thresholds, levels, n, &ap);
+  if (st != GRINQH_OK) return st;
+  return launch_vmm_fused(planes, scales, zeros, x, K, N, ap, y, workspace, as_stream(stream));
+}
+
+}  // extern "C"

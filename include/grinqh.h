@@ -1,0 +1,168 @@
+/*
+ * grinqh.h -- C ABI of the GRINQH decode-stage vector-matrix multiply for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "GRINQH: Graded Input-based Quantization Hierarchy for Efficient
+ * LLM Generation" (arXiv 2606.23419).  At batch size 1, y = x W over one
+ * linear layer, W stored input-major (row i = input channel i).  Each row i
+ * gets a bit width b_i in {0..8} from |x_i| and calibrated thresholds
+ * (section 3.1); only the b_i most significant bit planes of that row are
+ * read from a nested bit-plane store (section 3.3, Appendix C.1); the
+ * truncated code is rebuilt with the midpoint term and dequantised with the
+ * row group's scale and zero (section 3.3), and products accumulate in fp32.
+ *
+ * Conventions shared by every call below
+ * - Pointers are DEVICE pointers unless the argument says "host".  The caller
+ *   allocates and owns every buffer; the library allocates nothing and keeps
+ *   no state between calls.
+ * - fp16 values travel as their IEEE binary16 bit patterns (uint16_t).
+ * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *   enqueues work on it and returns without waiting for the device.
+ * - Arguments are validated on the host before any HIP call; a rejected call
+ *   returns GRINQH_EINVAL and enqueues nothing.  A failed launch returns
+ *   GRINQH_EDEVICE.  grinqh_last_error() then describes the failure.
+ * - Calls that share a workspace buffer must not overlap in time (run them
+ *   on one stream, or give each stream its own workspace).
+ *
+ * Store layout (this library's concrete form of the paper's bit-planar
+ * store; grinqh_layout_version() == 2):
+ * - N_pad = N rounded up to a multiple of 32.  Columns are cut into tiles of
+ *   GRINQH_TILE = 1024 columns; tile t has width C_t = min(1024, N_pad - 1024 t).
+ * - Tile t occupies bytes [1024 K t, 1024 K t + K C_t).  Inside it, row tile
+ *   (t, i) starts at 1024 K t + i C_t and holds planes 0..7 back to back,
+ *   C_t / 8 bytes each; plane p holds bit (7 - p) of the 8-bit code, so the
+ *   top b planes of a row are one contiguous span of b C_t / 8 bytes.
+ * - A plane is a run of little-endian 32-bit words, one per 32 columns.  In
+ *   the word for columns 32w .. 32w + 31 of the tile, column 32w + 4m + j
+ *   (m = 0..7, j = 0..3) sits at bit 8j + m.
+ * - Padding columns N .. N_pad - 1 hold code 0 and are never written to y.
+ *
+ * Scales and zeros: fp16 [G][N] row-major with G = ceil(K / 128); rows
+ * 128g .. 128g + 127 share s[g][j] and z[g][j] (section 4: group size 128).
+ */
+#ifndef GRINQH_H
+#define GRINQH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GRINQH_OK = 0,
+    GRINQH_EINVAL = -1,   /* bad argument; nothing was enqueued */
+    GRINQH_EDEVICE = -2   /* HIP reported an error (no device, launch failure) */
+};
+
+#define GRINQH_GROUP 128          /* rows per (scale, zero) group */
+#define GRINQH_TILE 1024          /* columns per row tile of the store */
+#define GRINQH_MAX_THRESHOLDS 8   /* n <= 8 thresholds, n + 1 <= 9 levels */
+#define GRINQH_MAX_BITS 8         /* b_max */
+
+/* Version of the store layout described above (2). */
+int grinqh_layout_version(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* grinqh_status_string(int status);
+
+/* Message for the most recent failed call on this host thread ("" if none). */
+const char* grinqh_last_error(void);
+
+/* Size in bytes of the bit-plane store for K rows and N columns: K * N_pad.
+ * Returns -1 if K <= 0 or N <= 0. */
+int64_t grinqh_planes_bytes(int64_t K, int64_t N);
+
+/* Workspace bytes grinqh_vmm / grinqh_decode_vmm need for a K x N layer
+ * (split-K partial sums and per-tile counters).  Returns -1 for K, N <= 0. */
+int64_t grinqh_workspace_bytes(int64_t K, int64_t N);
+
+/* Zero a workspace so it can be used by grinqh_vmm / grinqh_decode_vmm.
+ * Needed once after allocation: every successful VMM call leaves the
+ * counters at zero again.  Uses a fill kernel, so it may be captured in a
+ * HIP graph. */
+int grinqh_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Offline packing (section 3.3 "Storage Layout and Weight Loading";
+ * Appendix C.1 "Bit-packing", "Grouping").
+ * codes:  u8 [K][N] row-major, the b_max = 8 bit codes (row = input channel).
+ * planes: u8 [grinqh_planes_bytes(K, N)], written completely (padding too).
+ * Errors: EINVAL for NULL pointers or K, N <= 0 or K * N_pad >= 2^40.
+ */
+int grinqh_pack(const uint8_t* codes, int64_t K, int64_t N, uint8_t* planes, void* stream);
+
+/*
+ * Offline threshold calibration by percentile mapping (section 3.2;
+ * Appendix A.1 eq. (2)).
+ * calib:      fp16 [V][K] row-major, V calibration activation vectors.
+ * P:          host double [n_levels], the target share p_k of rows at level k.
+ * n_levels:   1 .. 9; n = n_levels - 1 thresholds are produced.
+ * thresholds: fp32 [n] (device).  theta_k = mean over vectors of the
+ *             linear-interpolation c_k-quantile of |v| with c_k = p_0 + ... +
+ *             p_{k-1} (position c_k (K - 1) between order statistics),
+ *             averaged in fp64 in vector order and rounded to fp32;
+ *             c_k <= 0 gives 0 and c_k >= 1 gives +inf.
+ * Errors: EINVAL for NULL pointers, V <= 0, K <= 0, n_levels outside 1..9,
+ * or a P entry that is negative or not finite.
+ */
+int grinqh_calibrate(const uint16_t* calib, int64_t V, int64_t K, const double* P, int n_levels,
+                     float* thresholds, void* stream);
+
+/*
+ * Dynamic precision assignment and active-row selection (section 3.1).
+ * x:          fp16 [K].
+ * thresholds: host fp32 [n], non-decreasing, >= 0 (+inf allowed), 0 <= n <= 8.
+ * levels:     host u8 [n + 1], each 0..8.
+ * bits:       u8 [K] out: b_i = levels[#{t : |x_i| >= thresholds[t]}] (fp32
+ *             compare; a tie goes to the upper level; NaN gets levels[0]).
+ * active_idx: i32 [K] out: the rows with b_i > 0 in ascending order in its
+ *             first *n_active entries (the rest is left untouched).
+ * n_active:   i32 [1] out.
+ * Errors: EINVAL for NULL pointers, K <= 0 or K >= 2^31, n outside 0..8,
+ * thresholds negative, NaN or decreasing, or a level above 8.
+ */
+int grinqh_assign_bits(const uint16_t* x, int64_t K, const float* thresholds, const uint8_t* levels,
+                       int n, uint8_t* bits, int32_t* active_idx, int32_t* n_active, void* stream);
+
+/*
+ * The decode-stage VMM from an explicit assignment (section 3.3).
+ * y[j] = sum over listed rows i of x_i (s[g][j] r_ij + z[g][j]), g = i / 128,
+ * r_ij = (q_ij with its low 8 - b_i bits cleared) + phi_i, phi_i = 2^(7 - b_i)
+ * for b_i < 8 and 0 for b_i = 8; only the top b_i planes of a row are read.
+ * planes:     the store (layout above) for K x N.
+ * scales, zeros: fp16 [ceil(K/128)][N].
+ * x:          fp16 [K].
+ * bits:       u8 [K]; entries above 8 are treated as 8, rows with 0 add nothing.
+ * active_idx: i32 [*n_active], strictly ascending, each in [0, K) -- for
+ *             example the output of grinqh_assign_bits.
+ * n_active:   i32 [1] on the device (read by the kernel; no host sync).
+ * y:          fp32 [N] out (written completely).
+ * workspace:  grinqh_workspace_bytes(K, N) bytes, zeroed once with
+ *             grinqh_workspace_init.
+ * Errors: EINVAL for NULL pointers, K, N <= 0, K >= 2^31, or a workspace
+ * smaller than grinqh_workspace_bytes(K, N).
+ */
+int grinqh_vmm(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+               const uint16_t* x, const uint8_t* bits, const int32_t* active_idx,
+               const int32_t* n_active, int64_t K, int64_t N, float* y,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The whole decode step in one launch: assignment (section 3.1) fused into
+ * the VMM (section 3.3).  Same result as grinqh_assign_bits followed by
+ * grinqh_vmm, without materialising bits or the active list.
+ * thresholds/levels/n as in grinqh_assign_bits (host arrays); the remaining
+ * arguments as in grinqh_vmm.
+ */
+int grinqh_decode_vmm(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                      const uint16_t* x, int64_t K, int64_t N,
+                      const float* thresholds, const uint8_t* levels, int n, float* y,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRINQH_H */

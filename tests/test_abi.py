@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host (these calls return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_stage_gemv_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grinqh.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(grinqh_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(g.LIB_PATH):
+        pytest.fail("libgrinqh.so is not built (run python -m decode_stage_gemv_amd.build)")
+    return g.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 11
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in g._SIGNATURES, name
+
+
+def test_static_queries(lib):
+    assert lib.grinqh_layout_version() == 2
+    assert lib.grinqh_status_string(0) == b"ok"
+    assert lib.grinqh_status_string(-1) == b"invalid argument"
+    assert lib.grinqh_status_string(-2) == b"device error"
+    assert lib.grinqh_planes_bytes(4096, 14336) == 4096 * 14336
+    assert lib.grinqh_planes_bytes(3, 33) == 3 * 64
+    assert lib.grinqh_planes_bytes(0, 5) == -1
+    assert lib.grinqh_workspace_bytes(-1, 5) == -1
+    assert lib.grinqh_workspace_bytes(128, 4096) >= 0
+    assert lib.grinqh_workspace_bytes(4096, 14336) >= 4 * 14336
+
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def _err(lib):
+    return lib.grinqh_last_error().decode()
+
+
+def test_pack_validation(lib):
+    assert lib.grinqh_pack(None, 4, 4, FAKE, None) == g.EINVAL
+    assert lib.grinqh_pack(FAKE, 0, 4, FAKE, None) == g.EINVAL
+    assert "positive" in _err(lib)
+    assert lib.grinqh_pack(FAKE, 4, -3, FAKE, None) == g.EINVAL
+
+
+def test_assign_validation(lib):
+    th = (ctypes.c_float * 4)(0.5, 1.0, 2.0, 4.0)
+    lv = (ctypes.c_uint8 * 5)(0, 2, 3, 4, 8)
+    args = lambda t, l, n, K=16: lib.grinqh_assign_bits(FAKE, K, ctypes.cast(t, ctypes.c_void_p),
+                                                        ctypes.cast(l, ctypes.c_void_p), n, FAKE, FAKE, FAKE, None)
+    assert args(th, lv, 9) == g.EINVAL
+    assert args(th, lv, -1) == g.EINVAL
+    assert args(th, lv, 4, K=0) == g.EINVAL
+    bad = (ctypes.c_float * 4)(0.5, 0.25, 2.0, 4.0)
+    assert args(bad, lv, 4) == g.EINVAL and "decrease" in _err(lib)
+    nan = (ctypes.c_float * 4)(float("nan"), 1.0, 2.0, 4.0)
+    assert args(nan, lv, 4) == g.EINVAL
+    neg = (ctypes.c_float * 4)(-1.0, 1.0, 2.0, 4.0)
+    assert args(neg, lv, 4) == g.EINVAL
+    badlv = (ctypes.c_uint8 * 5)(0, 2, 3, 9, 8)
+    assert args(th, badlv, 4) == g.EINVAL and "level" in _err(lib)
+    assert lib.grinqh_assign_bits(FAKE, 16, ctypes.cast(th, ctypes.c_void_p), ctypes.cast(lv, ctypes.c_void_p),
+                                  4, None, FAKE, FAKE, None) == g.EINVAL
+
+
+def test_vmm_validation(lib):
+    need = lib.grinqh_workspace_bytes(4096, 4096)
+    assert need > 0
+    r = lib.grinqh_vmm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 4096, FAKE, FAKE, need - 1, None)
+    assert r == g.EINVAL and "workspace" in _err(lib)
+    r = lib.grinqh_vmm(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4096, 4096, FAKE, FAKE, need, None)
+    assert r == g.EINVAL
+    r = lib.grinqh_vmm(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 4096, FAKE, FAKE, need, None)
+    assert r == g.EINVAL
+    th = (ctypes.c_float * 1)(1.0)
+    lv = (ctypes.c_uint8 * 2)(0, 12)
+    r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 4096, 4096, ctypes.cast(th, ctypes.c_void_p),
+                              ctypes.cast(lv, ctypes.c_void_p), 1, FAKE, FAKE, need, None)
+    assert r == g.EINVAL
+    r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 0, 4096, ctypes.cast(th, ctypes.c_void_p),
+                              ctypes.cast(lv, ctypes.c_void_p), 1, FAKE, FAKE, need, None)
+    assert r == g.EINVAL
+
+
+def test_calibrate_validation(lib):
+    P = (ctypes.c_double * 3)(0.3, 0.2, 0.5)
+    Pp = ctypes.cast(P, ctypes.c_void_p)
+    assert lib.grinqh_calibrate(FAKE, 0, 16, Pp, 3, FAKE, None) == g.EINVAL
+    assert lib.grinqh_calibrate(FAKE, 4, 16, Pp, 10, FAKE, None) == g.EINVAL
+    assert lib.grinqh_calibrate(FAKE, 4, 16, Pp, 0, FAKE, None) == g.EINVAL
+    neg = (ctypes.c_double * 3)(0.3, -0.2, 0.5)
+    assert lib.grinqh_calibrate(FAKE, 4, 16, ctypes.cast(neg, ctypes.c_void_p), 3, FAKE, None) == g.EINVAL
+    # one level: no thresholds to compute, nothing enqueued
+    assert lib.grinqh_calibrate(FAKE, 4, 16, Pp, 1, None, None) == g.OK
+
+
+def test_workspace_init_validation(lib):
+    assert lib.grinqh_workspace_init(None, 16, None) == g.EINVAL
+    assert lib.grinqh_workspace_init(None, 0, None) == g.OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(g, "_lib", None)
+    monkeypatch.setattr(g, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        g.lib()

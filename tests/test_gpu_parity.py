@@ -1,0 +1,252 @@
+"""Parity of the HIP library (through its C ABI) with the fp64 oracle.
+
+Bit-exact: packed planes, bit assignments, the active-row list and its
+length, calibrated thresholds.  Floating point: every output element within
+|y_gpu - y_ref| <= 1e-3 * sum_i |x_i w_hat_ij| + 1e-4 (the sum taken in fp64
+by the oracle).
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+torch = pytest.importorskip("torch")
+import decode_stage_gemv_amd as grq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-3
+ABS_TOL = 1e-4
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@functools.lru_cache(maxsize=8)
+def layer(K, N, config=0, matrix=0):
+    return synthetic.make_layer(K, N, config=config, matrix=matrix, n_test=2)
+
+
+def _check_y(y_gpu, codes, scales, zeros, x, bits, cols=None):
+    if cols is not None:
+        codes, scales, zeros = codes[:, cols], scales[:, cols], zeros[:, cols]
+        y_gpu = y_gpu[cols]
+    ref = oracle.vmm(codes, scales, zeros, x, bits)
+    mag = oracle.vmm_abs(codes, scales, zeros, x, bits)
+    err = np.abs(y_gpu.astype(np.float64) - ref)
+    bound = REL_TOL * mag + ABS_TOL
+    worst = int(np.argmax(err - bound))
+    assert np.all(err <= bound), f"col {worst}: gpu {y_gpu[worst]} ref {ref[worst]} err {err[worst]} bound {bound[worst]}"
+    return float(np.max(err / (mag + 1e-30)))
+
+
+def _run_decode(lay, x, th, levels):
+    K, N = lay.K, lay.N
+    planes = grq.pack(_dev(lay.codes))
+    ws = grq.make_workspace(K, N)
+    y = grq.decode_vmm(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), K, N, th, levels, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), planes, ws
+
+
+# --------------------------------------------------------------------------- pack
+
+@pytest.mark.parametrize("K,N", [(256, 256), (300, 70), (130, 1056), (7, 33), (2, 64), (129, 2100), (4096, 1024)])
+def test_pack_bit_exact(K, N):
+    codes = np.random.default_rng(K * 7 + N).integers(0, 256, size=(K, N), dtype=np.uint8)
+    got = grq.pack(_dev(codes)).cpu().numpy()
+    assert np.array_equal(got, oracle.pack(codes))
+
+
+def test_pack_bit_exact_full_size():
+    lay = layer(4096, 14336, 2, 4)
+    got = grq.pack(_dev(lay.codes)).cpu().numpy()
+    assert np.array_equal(got, oracle.pack(lay.codes))
+
+
+# ------------------------------------------------------------------ calibration
+
+@pytest.mark.parametrize("K,N,cfg,P", [
+    (256, 256, 0, synthetic.P_TINY),
+    (4096, 64, 1, synthetic.P_LEVELS_5[2]),
+    (4096, 64, 1, synthetic.P_LEVELS_5[3]),
+    (4096, 64, 1, synthetic.P_LEVELS_5[4]),
+    (4096, 64, 1, synthetic.P_LEVELS_5[8]),
+    (28672, 64, 4, synthetic.P_LEVELS_4[0.5]),
+    (7, 8, 5, (0.3, 0.0, 0.2, 0.5)),
+    (1, 8, 5, (0.5, 0.5)),
+])
+def test_calibrate_bit_exact(K, N, cfg, P):
+    calib = synthetic.make_calibration(K, config=cfg, matrix=0)
+    want = oracle.calibrate(calib, P)
+    got = grq.calibrate(_dev(calib), P).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (got, want)
+
+
+def test_calibrate_golden_vectors():
+    v = np.array([[1.0, -2.0, 3.0, -4.0, 5.0], [0.5, 0.5, 8.0, -1.0, 2.0]], np.float16)
+    got = grq.calibrate(_dev(v), (0.3, 0.2, 0.5)).cpu().numpy()
+    assert np.array_equal(got, oracle.calibrate(v, (0.3, 0.2, 0.5)))
+    assert got.tolist() == pytest.approx([1.4, 2.0], rel=1e-7)
+
+
+# ------------------------------------------------------------------- assignment
+
+def _assign_both(x, th, levels):
+    bits, idx, n = grq.assign_bits(_dev(x), th, levels)
+    torch.cuda.synchronize()
+    b_ref = oracle.assign(x, np.asarray(th, np.float32), levels)
+    i_ref, n_ref = oracle.compact(b_ref)
+    n_gpu = int(n.cpu().item())
+    assert np.array_equal(bits.cpu().numpy(), b_ref)
+    assert n_gpu == n_ref
+    assert np.array_equal(idx.cpu().numpy()[:n_gpu], i_ref)
+    return b_ref
+
+
+@pytest.mark.parametrize("K,cfg,P", [(256, 0, synthetic.P_TINY), (4096, 1, synthetic.P_LEVELS_5[3]),
+                                     (14336, 2, synthetic.P_LEVELS_5[2]), (20000, 3, synthetic.P_LEVELS_5[4]),
+                                     (28672, 4, synthetic.P_LEVELS_4[0.5]), (1, 0, synthetic.P_TINY)])
+def test_assign_bit_exact(K, cfg, P):
+    levels = synthetic.LEVELS_5 if len(P) == 5 else synthetic.LEVELS_4
+    th = oracle.calibrate(synthetic.make_calibration(K, config=cfg, matrix=0), P)
+    x = synthetic.make_activations(K, 1, config=cfg, matrix=0)[0]
+    _assign_both(x, th, levels)
+
+
+def test_assign_edge_cases():
+    th = [0.5, 1.0, 2.0, 4.0]
+    lv = (0, 2, 3, 4, 8)
+    ties = np.array([0.0, 0.25, 0.5, -0.5, 0.75, 1.0, -1.5, 2.0, -3.0, 4.0, -100.0, 65504.0,
+                     np.nan, np.inf, -np.inf, -0.0], np.float16)
+    b = _assign_both(ties, th, lv)
+    assert b[:12].tolist() == [0, 0, 2, 2, 2, 3, 3, 4, 4, 8, 8, 8]
+    x = synthetic.make_activations(3000, 1, config=7, matrix=0)[0]
+    _assign_both(x, [0.0] * 4, lv)
+    _assign_both(x, [float("inf")] * 4, lv)
+    _assign_both(x, [], (3,))
+    _assign_both(x, [1.0, 1.0, 1.0], (1, 2, 5, 7))
+    _assign_both(x, [0.3, 2.5], (2, 0, 8))       # level 0 may sit above 0
+
+
+# ------------------------------------------------------------------------- VMM
+
+CASES = [
+    # (K, N, config, matrix, P, levels)
+    (256, 256, 0, 0, synthetic.P_TINY, synthetic.LEVELS_5),
+    (4096, 4096, 1, 0, synthetic.P_LEVELS_5[2], synthetic.LEVELS_5),
+    (4096, 4096, 1, 0, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5),
+    (4096, 4096, 1, 0, synthetic.P_LEVELS_5[4], synthetic.LEVELS_5),
+    (4096, 4096, 1, 0, synthetic.P_LEVELS_5[8], synthetic.LEVELS_5),
+    (4096, 1024, 2, 1, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5),
+    (300, 70, 5, 0, synthetic.P_TINY, synthetic.LEVELS_5),
+    (129, 1100, 5, 1, synthetic.P_LEVELS_5[4], synthetic.LEVELS_5),
+    (1, 33, 5, 2, (0.0, 1.0), (0, 8)),
+    (4097, 1056, 5, 3, synthetic.P_LEVELS_4[1], synthetic.LEVELS_4),
+    (1000, 2080, 5, 4, synthetic.P_LEVELS_4[0.5], synthetic.LEVELS_4),
+]
+
+
+@pytest.mark.parametrize("K,N,cfg,mat,P,levels", CASES)
+def test_decode_vmm_parity(K, N, cfg, mat, P, levels):
+    lay = layer(K, N, cfg, mat)
+    th = oracle.calibrate(lay.calib, P)
+    x = lay.x[0]
+    y, planes, ws = _run_decode(lay, x, th, levels)
+    bits = oracle.assign(x, th, levels)
+    _check_y(y, lay.codes, lay.scales, lay.zeros, x, bits)
+    # the two-call path (assignment, then VMM from the list) gives the same bits
+    b, idx, n = grq.assign_bits(_dev(x), th, levels)
+    y2 = grq.vmm(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), b, idx, n, K, N, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().numpy().view(np.uint32), y.view(np.uint32))
+
+
+def test_vmm_from_oracle_assignment():
+    """grinqh_vmm does not need bits produced by grinqh_assign_bits."""
+    lay = layer(4096, 4096, 1, 0)
+    x = lay.x[1]
+    bits = np.random.default_rng(3).integers(0, 9, size=4096).astype(np.uint8)
+    idx, n = oracle.compact(bits)
+    planes = grq.pack(_dev(lay.codes))
+    ws = grq.make_workspace(4096, 4096)
+    idx_full = np.zeros(4096, np.int32)
+    idx_full[:n] = idx
+    y = grq.vmm(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), _dev(bits), _dev(idx_full),
+                _dev(np.array([n], np.int32)), 4096, 4096, ws)
+    torch.cuda.synchronize()
+    _check_y(y.cpu().numpy(), lay.codes, lay.scales, lay.zeros, x, bits)
+
+
+def test_vmm_list_subset():
+    """Only listed rows contribute, even where bits are non-zero elsewhere."""
+    lay = layer(1000, 2080, 5, 4)
+    x = lay.x[0]
+    bits = np.full(1000, 3, np.uint8)
+    listed = np.arange(0, 1000, 7, dtype=np.int32)
+    planes = grq.pack(_dev(lay.codes))
+    ws = grq.make_workspace(1000, 2080)
+    idx_full = np.zeros(1000, np.int32)
+    idx_full[:len(listed)] = listed
+    y = grq.vmm(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), _dev(bits), _dev(idx_full),
+                _dev(np.array([len(listed)], np.int32)), 1000, 2080, ws)
+    torch.cuda.synchronize()
+    eff = np.zeros(1000, np.uint8)
+    eff[listed] = 3
+    _check_y(y.cpu().numpy(), lay.codes, lay.scales, lay.zeros, x, eff)
+
+
+def test_all_eight_bits_equals_dense_gemv():
+    lay = layer(4096, 4096, 1, 0)
+    x = lay.x[0]
+    y, _, _ = _run_decode(lay, x, [0.0] * 4, synthetic.LEVELS_5)
+    bits = np.full(4096, 8, np.uint8)
+    _check_y(y, lay.codes, lay.scales, lay.zeros, x, bits)
+    g = np.arange(4096) // 128
+    dense = x.astype(np.float64) @ (lay.scales[g].astype(np.float64) * lay.codes + lay.zeros[g].astype(np.float64))
+    mag = oracle.vmm_abs(lay.codes, lay.scales, lay.zeros, x, bits)
+    assert np.all(np.abs(y - dense) <= REL_TOL * mag + ABS_TOL)
+
+
+def test_all_zero_bits_gives_zero():
+    lay = layer(4096, 1024, 2, 1)
+    y, _, _ = _run_decode(lay, lay.x[0], [float("inf")] * 4, synthetic.LEVELS_5)
+    assert np.array_equal(y, np.zeros(1024, np.float32))
+
+
+def test_deterministic_repeat():
+    lay = layer(4096, 4096, 1, 0)
+    th = oracle.calibrate(lay.calib, synthetic.P_LEVELS_5[3])
+    planes = grq.pack(_dev(lay.codes))
+    ws = grq.make_workspace(4096, 4096)
+    args = (planes, _dev(lay.scales), _dev(lay.zeros), _dev(lay.x[0]), 4096, 4096, th, synthetic.LEVELS_5, ws)
+    y1 = grq.decode_vmm(*args).cpu().numpy()
+    y2 = grq.decode_vmm(*args).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+
+
+# ------------------------------------------------- full sizes, sampled outputs
+
+FULL = [
+    (4096, 14336, 2, 4, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5),
+    (4096, 14336, 2, 4, synthetic.P_LEVELS_5[2], synthetic.LEVELS_5),
+    (14336, 4096, 2, 6, synthetic.P_LEVELS_5[4], synthetic.LEVELS_5),
+    (8192, 28672, 4, 0, synthetic.P_LEVELS_4[0.5], synthetic.LEVELS_4),
+    (28672, 8192, 4, 1, synthetic.P_LEVELS_4[8], synthetic.LEVELS_4),
+]
+
+
+@pytest.mark.parametrize("K,N,cfg,mat,P,levels", FULL)
+def test_full_size_sampled_columns(K, N, cfg, mat, P, levels):
+    lay = layer(K, N, cfg, mat)
+    th = oracle.calibrate(lay.calib, P)
+    x = lay.x[0]
+    y, _, _ = _run_decode(lay, x, th, levels)
+    bits = oracle.assign(x, th, levels)
+    r = np.random.default_rng(K + N)
+    cols = np.unique(np.concatenate([r.choice(N, 192, replace=False), [0, 31, 32, 1023, 1024, N - 1]]))
+    _check_y(y, lay.codes, lay.scales, lay.zeros, x, bits, cols)
