@@ -53,7 +53,7 @@ def _P(key, levels):
 class Prepared:
     """A layer resident on the GPU in R rotated copies, thresholds calibrated on the GPU."""
 
-    def __init__(self, name):
+    def __init__(self, name, mode="decode"):
         import torch
         import synthetic
         import decode_stage_gemv_amd as grq
@@ -79,6 +79,8 @@ class Prepared:
         del planes
         self.ws = grq.make_workspace(K, N)
         self.y = torch.empty(N, dtype=torch.float32, device=dev)
+        self.mode = mode
+        self.ybufs = [torch.zeros(N, dtype=torch.float32, device=dev) for _ in range(2)]
         # algorithmic bytes of each copy's step, from the GPU's own assignment
         self.bytes = []
         self.avg_bits = []
@@ -100,25 +102,75 @@ class Prepared:
     def step(self, k):
         import decode_stage_gemv_amd as grq
         planes, scales, zeros, x = self.copies[k % self.R]
-        grq.decode_vmm(planes, scales, zeros, x, self.K, self.N, self.thresholds, self.levels,
-                       self.ws, out=self.y)
+        if self.mode == "accumulate":
+            # decode-loop ping-pong: add into one buffer, clear the other for the next step
+            grq.decode_vmm_accumulate(planes, scales, zeros, x, self.K, self.N, self.thresholds,
+                                      self.levels, self.ybufs[k % 2], self.ybufs[(k + 1) % 2])
+        else:
+            grq.decode_vmm(planes, scales, zeros, x, self.K, self.N, self.thresholds, self.levels,
+                           self.ws, out=self.y)
 
-    def run(self, steps, warmup):
+    def run(self, steps, warmup, graph=True):
+        """Time `steps` back-to-back steps; returns (ms per step, bytes per step).
+
+        With graph=True the steps are captured once into a HIP graph and the
+        timed region is one replay (no host launch overhead between steps).
+        Events are recorded on the stream the kernels run on.
+        """
         import torch
         for k in range(warmup):
             self.step(k)
         torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for k in range(steps):
-            self.step(k)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(stop) / steps
+        if graph:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    for k in range(steps):
+                        self.step(k)
+                g.replay()                      # warm replay
+                s.synchronize()
+                start = torch.cuda.Event(enable_timing=True)
+                stop = torch.cuda.Event(enable_timing=True)
+                start.record(s)
+                g.replay()
+                stop.record(s)
+                s.synchronize()
+            ms = start.elapsed_time(stop) / steps
+        else:
+            stream = torch.cuda.current_stream()
+            start = torch.cuda.Event(enable_timing=True)
+            stop = torch.cuda.Event(enable_timing=True)
+            start.record(stream)
+            for k in range(steps):
+                self.step(k)
+            stop.record(stream)
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(stop) / steps
         step_bytes = float(np.mean([self.bytes[k % self.R] for k in range(steps)]))
         return ms, step_bytes
+
+
+def copy_probe(nbytes=512 << 20, reps=20):
+    """A plain device-to-device copy of known size: reads nbytes, writes nbytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"copy_probe": {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms,
+                                     "GB_s_read_plus_write": gbs}}), flush=True)
 
 
 def cpu_baseline(prep, budget_s=15.0):
@@ -149,6 +201,12 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--sweep", action="store_true", help="also time the bit-width sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
+    ap.add_argument("--mode", choices=["decode", "accumulate"], default="decode",
+                    help="decode: grinqh_decode_vmm (deterministic split-K); "
+                         "accumulate: grinqh_decode_vmm_accumulate (fp32 atomics, ping-pong outputs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="time a plain 512 MiB device copy (reference for bandwidth and counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode VMM path here is single-GPU "
@@ -159,15 +217,20 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
-    prep = Prepared(args.workload)
-    ms, step_bytes = prep.run(args.steps, args.warmup)
+    if args.copy_probe:
+        copy_probe()
+        return
+    prep = Prepared(args.workload, args.mode)
+    ms, step_bytes = prep.run(args.steps, args.warmup, graph=not args.no_graph)
+    if args.no_graph:
+        log("host-launched steps (no graph): includes Python and ctypes launch overhead")
     gbs = step_bytes / (ms * 1e-3) / 1e9
     log(f"{args.workload}: {ms * 1e3:.2f} us/VMM, {gbs:.1f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
 
     sweep = {}
     if args.sweep:
         for name in SWEEP:
-            p = Prepared(name)
+            p = Prepared(name, args.mode)
             m, b = p.run(args.steps, args.warmup)
             sweep[name] = {"us_per_vmm": m * 1e3, "GB_s": b / (m * 1e-3) / 1e9,
                            "frac_of_peak": b / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -191,7 +254,7 @@ def main():
         "vs_baseline": None,
         "dtype": "u8 planes, fp16 x/scale/zero, fp32 accumulate",
         "data": "synthetic (seeded N(0,0.02) weights, RTN 8-bit, log-normal x with 1% outlier channels)",
-        "config": {"workload": args.workload, "K": prep.K, "N": prep.N,
+        "config": {"workload": args.workload, "entry_point": "grinqh_decode_vmm" if args.mode == "decode" else "grinqh_decode_vmm_accumulate", "K": prep.K, "N": prep.N,
                    "avg_bits": float(np.mean(prep.avg_bits)), "bytes_per_step": step_bytes,
                    "rotated_copies": prep.R, "thresholds": prep.thresholds, "levels": list(prep.levels)},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

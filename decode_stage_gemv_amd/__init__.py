@@ -8,7 +8,8 @@ memory and streams.  There is no fallback: if the library is missing, every
 call raises.
 
 Names follow the C ABI in ``include/grinqh.h``:
-``pack``, ``calibrate``, ``assign_bits``, ``vmm``, ``decode_vmm``.
+``pack``, ``calibrate``, ``assign_bits``, ``vmm``, ``decode_vmm``,
+``decode_vmm_accumulate``.
 """
 from __future__ import annotations
 
@@ -53,6 +54,7 @@ _SIGNATURES = {
     "grinqh_assign_bits": ([_vp, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
     "grinqh_vmm": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp], _i32),
     "grinqh_decode_vmm": ([_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
+    "grinqh_decode_vmm_accumulate": ([_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
 }
 
 
@@ -219,3 +221,19 @@ def decode_vmm(planes, scales, zeros, x, K: int, N: int, thresholds: Sequence[fl
         ctypes.cast(th, _vp), ctypes.cast(lv, _vp), n, out.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out
+
+
+def decode_vmm_accumulate(planes, scales, zeros, x, K: int, N: int, thresholds: Sequence[float],
+                          levels: Sequence[int], y, clear=None, stream=None):
+    """y += the fused decode step's product (fp32 atomics, no workspace); zeroes `clear` if given."""
+    import torch
+    _check_layer(planes, scales, zeros, x, K, N)
+    _dev(y, "y", torch.float32, (N,))
+    if clear is not None:
+        _dev(clear, "clear", torch.float32, (N,))
+    th, lv, n = _host_thresholds(thresholds, levels)
+    _check("grinqh_decode_vmm_accumulate", lib().grinqh_decode_vmm_accumulate(
+        planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), x.data_ptr(), K, N,
+        ctypes.cast(th, _vp), ctypes.cast(lv, _vp), n, y.data_ptr(),
+        clear.data_ptr() if clear is not None else None, _stream(stream)))
+    return y

@@ -45,12 +45,19 @@ static int check_assign_params(const float* thresholds, const uint8_t* levels, i
   return GRINQH_OK;
 }
 
-static int check_vmm_common(const void* planes, const void* scales, const void* zeros, const void* x,
-                            const void* y, int64_t K, int64_t N, const void* ws, size_t ws_bytes) {
+static int check_layer(const void* planes, const void* scales, const void* zeros, const void* x,
+                       const void* y, int64_t K, int64_t N) {
   if (!planes || !scales || !zeros || !x || !y) return fail(GRINQH_EINVAL, "NULL data pointer");
   if (K <= 0 || N <= 0) return fail(GRINQH_EINVAL, "K = %lld, N = %lld must be positive", (long long)K, (long long)N);
   if (K >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "K or N too large");
   if (K * padded_cols(N) >= (int64_t(1) << 40)) return fail(GRINQH_EINVAL, "store larger than 2^40 bytes");
+  return GRINQH_OK;
+}
+
+static int check_vmm_common(const void* planes, const void* scales, const void* zeros, const void* x,
+                            const void* y, int64_t K, int64_t N, const void* ws, size_t ws_bytes) {
+  const int st = check_layer(planes, scales, zeros, x, y, K, N);
+  if (st != GRINQH_OK) return st;
   const VmmGeometry g = vmm_geometry(K, N);
   if (!ws && g.bytes > 0) return fail(GRINQH_EINVAL, "workspace is NULL");
   if ((int64_t)ws_bytes < g.bytes)
@@ -158,6 +165,24 @@ int grinqh_decode_vmm(const uint8_t* planes, const uint16_t* scales, const uint1
   st = check_assign_params(thresholds, levels, n, &ap);
   if (st != GRINQH_OK) return st;
   return launch_vmm_fused(planes, scales, zeros, x, K, N, ap, y, workspace, as_stream(stream));
+}
+
+int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                                 const uint16_t* x, int64_t K, int64_t N,
+                                 const float* thresholds, const uint8_t* levels, int n,
+                                 float* y, float* clear, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_layer(planes, scales, zeros, x, y, K, N);
+  if (st != GRINQH_OK) return st;
+  if (clear) {
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(clear), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t len = (uintptr_t)N * sizeof(float);
+    if (c0 < y0 + len && y0 < c0 + len) return fail(GRINQH_EINVAL, "clear overlaps y");
+  }
+  AssignParams ap;
+  st = check_assign_params(thresholds, levels, n, &ap);
+  if (st != GRINQH_OK) return st;
+  return launch_vmm_accumulate(planes, scales, zeros, x, K, N, ap, y, clear, as_stream(stream));
 }
 
 }  // extern "C"

@@ -74,6 +74,9 @@ int launch_vmm_list(const uint8_t* planes, const uint16_t* scales, const uint16_
 int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                      const uint16_t* x, int64_t K, int64_t N, const AssignParams& ap, float* y,
                      void* ws, hipStream_t s);
+int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                          const uint16_t* x, int64_t K, int64_t N, const AssignParams& ap, float* y,
+                          float* clear, hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 }  // namespace grinqh

@@ -1,26 +1,47 @@
 // Decode-stage VMM over the bit-plane store (GRINQH paper, section 3.3
 // "Weight Reconstruction and Bias Correction"; Appendix C.1).
 //
-// Work split: a workgroup owns one column tile (<= 1024 columns) and one
-// 128-row group of K, so every row it touches shares one (scale, zero) row.
-// Its 8 half-waves (32 lanes each) take the group's active rows in turn; a
-// lane owns one 32-column plane word, loads only the b_i planes a row needs
-// and rebuilds the 32 truncated codes with rotate/AND-OR.  With the group
-// factored out,
+// Work split.  A workgroup owns one column tile (<= 1024 columns, one row
+// tile of the store per row) and one 128-row group of K, so every row it
+// touches shares one (scale, zero) row.  Its active rows are sorted by bit
+// width and taken two at a time; each 32-lane group of the workgroup owns a
+// stream of row pairs, and lane l of a group owns plane word l (32 columns).
+//
+// Per row pair and lane: the b planes of each row are fetched with buffer
+// loads whose offset is pushed out of range for planes the row does not need
+// (they return 0 and move no data), so every iteration issues the same number
+// of loads and the next pair's loads are in flight while the current pair is
+// computed.  The codes come back from the planes through a bit-transpose
+// network specialised for b (bitplane.hpp); byte j of code word m from the two
+// rows is paired into one fp16x2 operand (the code as an fp16 subnormal,
+// c * 2^-24) and v_dot2 multiplies it by the pair's fp16 activations, adding
+// into an fp32 accumulator: one dot per two weights.  With the group factored
+// out,
 //   sum_i x_i (s r_ij + z) = s (A_j + H) + z X,
 //   A_j = sum_i x_i (q_ij with low 8-b_i bits cleared),
 //   H = sum_i x_i phi_i,  X = sum_i x_i,
-// so the per-weight work is one convert and one FMA.  Half-wave partials
-// meet in LDS; workgroups of the same tile meet through a workspace of
-// partial rows, and the last one to arrive (per-tile counter) adds them in a
-// fixed order, so y does not depend on scheduling.
+// so the scale and zero are applied once per column per workgroup.
+//
+// Reduction across workgroups of a tile (split K): each workgroup writes one
+// partial row; the last to arrive (per-tile counter) adds them in split order
+// and writes y, so y does not depend on scheduling.
+#include <stdlib.h>
+
+#include "bitplane.hpp"
 #include "common.hpp"
 
 namespace grinqh {
 
-constexpr int kVmmThreads = 256;
-constexpr int kHalfWaves = kVmmThreads / 32;
+constexpr int kVmmThreads = 512;
+constexpr int kWaves = kVmmThreads / 64;
+constexpr int kLaneGroups = kVmmThreads / 32;
 constexpr int kRowsPerWG = kGroup;
+constexpr uint32_t kOutOfRange = 0x7FFFFF00u;   // buffer offset beyond any tile block
+constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw 32-bit buffer, gfx9 family
+
+constexpr int kScopeDevice = 16;              // cache-policy bits: sc1 = device scope
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 VmmGeometry vmm_geometry(int64_t K, int64_t N) {
   VmmGeometry g;
@@ -42,14 +63,13 @@ struct VmmArgs {
   const int32_t* active_idx;
   const int32_t* n_active;
   float* y;
+  float* clear;
   float* partials;
   unsigned* counters;
   int64_t K, N;
   int splits, tiles;
   AssignParams ap;
 };
-
-__device__ inline uint32_t rotr(uint32_t w, int s) { return __builtin_amdgcn_alignbit(w, w, s); }
 
 // First position p in [0, n) with idx[p] >= key (n if none); one full wave.
 __device__ int64_t wave_lower_bound(const int32_t* __restrict__ idx, int64_t n, int64_t key) {
@@ -78,16 +98,80 @@ __device__ int64_t wave_lower_bound(const int32_t* __restrict__ idx, int64_t n, 
   return lo;
 }
 
-template <bool kFused>
-__global__ __launch_bounds__(kVmmThreads) void vmm_group_kernel(VmmArgs a) {
+// One row pair's plane words and activations.
+struct PairRegs {
+  uint32_t w1[8], w2[8];
+  uint32_t xp;     // fp16 x of row 1 (low half) and row 2 (high half)
+  int b1, b2;
+};
+
+__device__ inline void issue_pair(__amdgpu_buffer_rsrc_t rsrc, int q, int npairs, int m,
+                                  const int* s_row, const int* s_bits, const uint16_t* s_xh,
+                                  int ct, uint32_t lane_off, bool lane_ok, PairRegs& r) {
+  int r1 = 0, r2 = 0, b1 = 0, b2 = 0;
+  uint32_t x1 = 0, x2 = 0;
+  if (q < npairs) {
+    const int e1 = 2 * q, e2 = 2 * q + 1;
+    r1 = s_row[e1];
+    b1 = s_bits[e1];
+    x1 = s_xh[e1];
+    if (e2 < m) {
+      r2 = s_row[e2];
+      b2 = s_bits[e2];
+      x2 = s_xh[e2];
+    }
+  }
+  if (!lane_ok) b1 = b2 = 0;
+  const uint32_t ps = (uint32_t)ct / 8;
+  const uint32_t base1 = (uint32_t)r1 * (uint32_t)ct + lane_off;
+  const uint32_t base2 = (uint32_t)r2 * (uint32_t)ct + lane_off;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t o1 = p < b1 ? base1 + (uint32_t)p * ps : kOutOfRange;
+    const uint32_t o2 = p < b2 ? base2 + (uint32_t)p * ps : kOutOfRange;
+    r.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)o1, 0, 0);
+    r.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)o2, 0, 0);
+  }
+  r.xp = x1 | (x2 << 16);
+  r.b1 = b1;
+  r.b2 = b2;
+}
+
+__device__ inline void compute_pair(const PairRegs& r, float (&acc)[32]) {
+  if ((r.b1 | r.b2) == 0) return;
+  uint32_t d1[8], d2[8];
+  planes_to_codes_rt(r.b1, r.w1, d1);
+  planes_to_codes_rt(r.b2, r.w2, d2);
+  const half2_t xv = __builtin_bit_cast(half2_t, r.xp);
+#pragma unroll
+  for (int mm = 0; mm < 8; ++mm) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // bytes: [row1 code, 0, row2 code, 0] -> two fp16 subnormals c * 2^-24
+      const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
+      const uint32_t pr = __builtin_amdgcn_perm(d2[mm], d1[mm], sel);
+      acc[4 * mm + j] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr), xv, acc[4 * mm + j], false);
+    }
+  }
+}
+
+// Output modes.
+enum : int {
+  kOutSplitK = 0,     // partial rows + last-arriving workgroup adds them in split order
+  kOutAccumulate = 1  // fp32 device-scope atomic adds into y (y += x W)
+};
+
+template <bool kFused, int kOut>
+__global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
   __shared__ int s_row[kRowsPerWG];
   __shared__ int s_bits[kRowsPerWG];
-  __shared__ float s_x[kRowsPerWG];
-  __shared__ int s_wcount[2];
+  __shared__ uint16_t s_xh[kRowsPerWG];
+  __shared__ int s_cnt[2][9];
   __shared__ int s_m;
-  __shared__ float s_hx[4][2];
+  __shared__ int s_p0;
+  __shared__ float s_hx[2][2];
   __shared__ int s_last;
-  __shared__ float s_red[kHalfWaves * kTile];
+  __shared__ float s_red[kLaneGroups * 32 * 33];
 
   const int tile = blockIdx.x % a.tiles;
   const int split = blockIdx.x / a.tiles;
@@ -99,64 +183,81 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_group_kernel(VmmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
+  const int64_t g = split;   // one 128-row group per workgroup
 
-  // ---- active rows of [k0, k1), ascending, into LDS
-  if constexpr (kFused) {
-    uint32_t b = 0;
-    float xf = 0.0f;
-    int before = 0;
-    if (wid < 2) {
-      const int64_t i = k0 + tid;
-      if (i < k1) {
-        const uint16_t xh = a.x[i];
-        b = level_bits(level_of(xh, a.ap), a.ap);
-        xf = half_bits_to_float(xh);
+  // ---- scale and zero of this thread's two output columns (tid, tid + 512),
+  // fetched now so their latency hides behind the rest of the work
+  uint16_t sc[2] = {0, 0}, zr[2] = {0, 0};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int col = tid + u * kVmmThreads;
+    if (col < ct && t0 + col < a.N) {
+      sc[u] = a.scales[g * a.N + t0 + col];
+      zr[u] = a.zeros[g * a.N + t0 + col];
+    }
+  }
+  if constexpr (kOut == kOutAccumulate) {
+    // the caller's next output buffer, zeroed once per column (split 0 only)
+    if (a.clear && split == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int col = tid + u * kVmmThreads;
+        if (col < ct && t0 + col < a.N) a.clear[t0 + col] = 0.0f;
       }
-      const uint64_t mask = __ballot(b > 0);
-      before = __popcll(mask & ((1ull << lane) - 1ull));
-      if (lane == 0) s_wcount[wid] = __popcll(mask);
     }
-    __syncthreads();
-    if (wid < 2 && b > 0) {
-      const int pos = (wid == 1 ? s_wcount[0] : 0) + before;
-      s_row[pos] = tid;
-      s_bits[pos] = (int)b;
-      s_x[pos] = xf;
-    }
-    if (tid == 0) s_m = s_wcount[0] + s_wcount[1];
-  } else {
+  }
+
+  // ---- gather this group's candidate rows: thread t < 128 holds one
+  if constexpr (!kFused) {
     if (wid == 0) {
       const int64_t n = *a.n_active;
       const int64_t p0 = wave_lower_bound(a.active_idx, n, k0);
       const int64_t p1 = wave_lower_bound(a.active_idx, n, k1);
       int m = (int)(p1 - p0);
       m = m < 0 ? 0 : (m > kRowsPerWG ? kRowsPerWG : m);
-      for (int r = lane; r < m; r += 64) {
-        const int64_t i = a.active_idx[p0 + r];
-        const bool inside = i >= k0 && i < k1;   // a well-formed list always is
-        uint32_t b = inside ? a.bits[i] : 0u;
-        b = b > 8u ? 8u : b;
-        s_row[r] = inside ? (int)(i - k0) : 0;
-        s_bits[r] = (int)b;
-        s_x[r] = inside ? half_bits_to_float(a.x[i]) : 0.0f;
+      if (lane == 0) {
+        s_m = m;
+        s_p0 = (int)p0;
       }
-      if (lane == 0) s_m = m;
+    }
+    __syncthreads();
+  }
+  uint32_t b = 0;
+  uint16_t xh = 0;
+  int rloc = 0;
+  if (wid < 2) {
+    if constexpr (kFused) {
+      rloc = tid;
+      if (k0 + tid < k1) {
+        xh = a.x[k0 + tid];
+        b = level_bits(level_of(xh, a.ap), a.ap);
+      }
+    } else {
+      if (tid < s_m) {
+        const int64_t i = a.active_idx[s_p0 + tid];
+        if (i >= k0 && i < k1) {   // a well-formed list always is
+          rloc = (int)(i - k0);
+          b = a.bits[i];
+          b = b > 8u ? 8u : b;
+          xh = a.x[i];
+        }
+      }
     }
   }
-  __syncthreads();
-  const int m = s_m;
 
-  // ---- H = sum x phi and X = sum x over the active rows (fixed order)
-  {
-    float h = 0.0f, xs = 0.0f;
-    if (tid < m) {
-      const int b = s_bits[tid];
-      const float xf = s_x[tid];
-      if (b > 0) {
-        xs = xf;
-        h = b < 8 ? xf * (float)(1 << (7 - b)) : 0.0f;
-      }
+  // ---- stable counting sort of active rows by bit width (1..8)
+  uint64_t my_mask = 0;
+  if (wid < 2) {
+#pragma unroll
+    for (int v = 1; v <= 8; ++v) {
+      const uint64_t mv = __ballot(b == (uint32_t)v);
+      if (lane == 0) s_cnt[wid][v] = __popcll(mv);
+      if (b == (uint32_t)v) my_mask = mv;
     }
+    // H = sum x phi and X = sum x over active rows (fixed butterfly order)
+    const float xf = half_bits_to_float(xh);
+    float h = (b > 0 && b < 8) ? xf * (float)(1 << (7 - (b > 0 ? b : 1))) : 0.0f;
+    float xs = b > 0 ? xf : 0.0f;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       h += __shfl_xor(h, off, 64);
@@ -167,96 +268,170 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_group_kernel(VmmArgs a) {
       s_hx[wid][1] = xs;
     }
   }
+  __syncthreads();
+  if (wid < 2 && b > 0) {
+    int pos = (wid == 1) ? s_cnt[0][b] : 0;
+    for (int v = 1; v < (int)b; ++v) pos += s_cnt[0][v] + s_cnt[1][v];
+    pos += __popcll(my_mask & ((1ull << lane) - 1ull));
+    s_row[pos] = rloc;
+    s_bits[pos] = (int)b;
+    s_xh[pos] = xh;
+  }
+  if (tid == 0) {
+    int m = 0;
+    for (int v = 1; v <= 8; ++v) m += s_cnt[0][v] + s_cnt[1][v];
+    s_m = m;
+  }
+  __syncthreads();
+  const int m = s_m;
 
-  // ---- plane streaming, rebuild, FMA
-  const int hw = tid >> 5;
-  const int hl = tid & 31;
-  const bool col_ok = hl < ct / 32;
-  const uint8_t* tile_base = a.planes + t0 * a.K;
-  const int plane_stride = ct / 8;
+  // ---- stream row pairs: lane group lg takes pairs lg, lg + 16, lg + 32,
+  // lg + 48 (at most 64 pairs per group), three in flight at a time
+  const int lg = tid >> 5;
+  const int ll = tid & 31;
+  const bool lane_ok = ll < ct / 32;
+  // Descriptor over this group's row tiles only: row r of the group starts at r * ct.
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.planes + t0 * a.K + k0 * ct), (short)0, (int)((k1 - k0) * ct), (int)kRsrcWord3);
+  const uint32_t lane_off = 4u * (uint32_t)ll;
+  const int npairs = (m + 1) / 2;
   float acc[32];
 #pragma unroll
   for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
-
-  for (int e = hw; e < m; e += kHalfWaves) {
-    const int r = s_row[e];
-    const int b = s_bits[e];
-    const float xf = s_x[e];
-    const uint8_t* rowp = tile_base + (k0 + r) * ct + 4 * hl;
-    uint32_t w[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      w[p] = 0u;
-      if (p < b && col_ok) w[p] = *reinterpret_cast<const uint32_t*>(rowp + p * plane_stride);
-    }
-#pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
-      uint32_t d = 0u;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) d |= rotr(w[p], (mm + p - 7) & 31) & (0x01010101u << (7 - p));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[4 * mm + j] += xf * (float)((d >> (8 * j)) & 0xFFu);
-    }
+  {
+    PairRegs p0, p1, p2;
+    issue_pair(rsrc, lg, npairs, m, s_row, s_bits, s_xh, ct, lane_off, lane_ok, p0);
+    issue_pair(rsrc, lg + kLaneGroups, npairs, m, s_row, s_bits, s_xh, ct, lane_off, lane_ok, p1);
+    issue_pair(rsrc, lg + 2 * kLaneGroups, npairs, m, s_row, s_bits, s_xh, ct, lane_off, lane_ok, p2);
+    compute_pair(p0, acc);
+    issue_pair(rsrc, lg + 3 * kLaneGroups, npairs, m, s_row, s_bits, s_xh, ct, lane_off, lane_ok, p0);
+    compute_pair(p1, acc);
+    compute_pair(p2, acc);
+    compute_pair(p0, acc);
   }
 
-  // ---- reduce half-waves, dequantise with the group's scale and zero
+  // ---- reduce the 16 lane groups in LDS (row stride 33 keeps both the
+  // writes and the column-wise reads free of bank conflicts).  A half-wave
+  // swap (v_permlane32_swap) would halve this, but this toolchain drops one of
+  // the swap's two results, so it is not used.
+  {
+    float* dst = s_red + (lg * 32 + ll) * 33;
 #pragma unroll
-  for (int c = 0; c < 32; ++c) s_red[hw * kTile + hl * 32 + c] = acc[c];
+    for (int c = 0; c < 32; ++c) dst[c] = acc[c];
+  }
   __syncthreads();
-  const float H = s_hx[0][0] + s_hx[1][0] + s_hx[2][0] + s_hx[3][0];
-  const float X = s_hx[0][1] + s_hx[1][1] + s_hx[2][1] + s_hx[3][1];
-  const int64_t g = k0 / kGroup;
-  for (int col = tid; col < ct; col += kVmmThreads) {
-    const int64_t gc = t0 + col;
-    float val = 0.0f;
-    if (m > 0 && gc < a.N) {
+  const float H = s_hx[0][0] + s_hx[1][0];
+  const float X = s_hx[0][1] + s_hx[1][1];
+  float val[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int col = tid + u * kVmmThreads;
+    if (m > 0 && col < ct && t0 + col < a.N) {
       float A = 0.0f;
 #pragma unroll
-      for (int h = 0; h < kHalfWaves; ++h) A += s_red[h * kTile + col];
-      const float s = half_bits_to_float(a.scales[g * a.N + gc]);
-      const float z = half_bits_to_float(a.zeros[g * a.N + gc]);
-      val = s * (A + H) + z * X;
-    }
-    if (a.splits == 1) {
-      if (gc < a.N) a.y[gc] = val;
-    } else {
-      a.partials[(int64_t)split * Np + gc] = val;
+      for (int h = 0; h < kLaneGroups; ++h) A += s_red[(h * 32 + (col >> 5)) * 33 + (col & 31)];
+      A *= 16777216.0f;   // codes entered as c * 2^-24
+      val[u] = half_bits_to_float(sc[u]) * (A + H) + half_bits_to_float(zr[u]) * X;
     }
   }
-  if (a.splits == 1) return;
 
-  // ---- last workgroup of the tile adds the partial rows in split order
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned old = atomicAdd(&a.counters[tile], 1u);
-    s_last = (old == (unsigned)(a.splits - 1)) ? 1 : 0;
+  if constexpr (kOut == kOutAccumulate) {
+    if (m > 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int col = tid + u * kVmmThreads;
+        if (col < ct && t0 + col < a.N)
+          __hip_atomic_fetch_add(a.y + t0 + col, val[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    return;
+  } else {
+    if (a.splits == 1) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int col = tid + u * kVmmThreads;
+        if (col < ct && t0 + col < a.N) a.y[t0 + col] = val[u];
+      }
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int col = tid + u * kVmmThreads;
+      // device-scope store: written through to the point where every XCD sees it
+      if (col < ct)
+        __hip_atomic_store(a.partials + (int64_t)split * Np + t0 + col, val[u], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- the last workgroup of the tile adds the partial rows in split
+    // order.  No cache-wide fence: each wave waits until its device-scope
+    // stores are acknowledged, the barrier makes that true for the whole
+    // workgroup, and only then is the tile counter bumped; the workgroup that
+    // sees the final count reads the partial rows with device-scope loads.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const unsigned old = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (old == (unsigned)(a.splits - 1)) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.partials + t0), (short)0, (int)(a.splits * Np * 4), (int)kRsrcWord3);
+    const uint32_t row_bytes = (uint32_t)(Np * 4);
+    float sum[2] = {0.0f, 0.0f};
+    // 32 splits per round, all loads of a round in flight together; splits
+    // past the end read as zero (out-of-range offsets)
+    for (int sp0 = 0; sp0 < a.splits; sp0 += 32) {
+      uint32_t v[32][2];
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int col = tid + e * kVmmThreads;
+          const bool ok = sp0 + u < a.splits && col < ct;
+          const uint32_t off = ok ? (uint32_t)(sp0 + u) * row_bytes + 4u * (uint32_t)col : kOutOfRange;
+          v[u][e] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, kScopeDevice);
+        }
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        sum[0] += __builtin_bit_cast(float, v[u][0]);
+        sum[1] += __builtin_bit_cast(float, v[u][1]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int col = tid + e * kVmmThreads;
+      if (col < ct && t0 + col < a.N) a.y[t0 + col] = sum[e];
+    }
+    if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int col = tid; col < ct; col += kVmmThreads) {
-    const int64_t gc = t0 + col;
-    if (gc >= a.N) continue;
-    float sum = 0.0f;
-    for (int sp = 0; sp < a.splits; ++sp) sum += a.partials[(int64_t)sp * Np + gc];
-    a.y[gc] = sum;
-  }
-  if (tid == 0) a.counters[tile] = 0u;
 }
 
-static int launch_vmm(bool fused, VmmArgs& a, void* ws, hipStream_t s) {
+static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_t s) {
   const VmmGeometry g = vmm_geometry(a.K, a.N);
+  if (g.partial_floats * 4 >= (int64_t)kOutOfRange)
+    return fail(GRINQH_EINVAL, "K x N too large for one split-K workspace (%lld partial floats)",
+                (long long)g.partial_floats);
   a.splits = (int)g.splits;
   a.tiles = (int)g.tiles;
   a.partials = reinterpret_cast<float*>(ws);
-  a.counters = g.bytes > 0 ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + g.counter_offset) : nullptr;
-  const int64_t grid = g.splits * g.tiles;
-  if (fused)
-    hipLaunchKernelGGL(vmm_group_kernel<true>, dim3((unsigned)grid), dim3(kVmmThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(vmm_group_kernel<false>, dim3((unsigned)grid), dim3(kVmmThreads), 0, s, a);
-  return check_launch(fused ? "grinqh_decode_vmm" : "grinqh_vmm");
+  a.counters = g.bytes > 0 && ws ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + g.counter_offset) : nullptr;
+  const dim3 grid((unsigned)(g.splits * g.tiles));
+  const dim3 block(kVmmThreads);
+  if (out_mode == kOutAccumulate) {
+    if (fused)
+      hipLaunchKernelGGL((vmm_kernel<true, kOutAccumulate>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((vmm_kernel<false, kOutAccumulate>), grid, block, 0, s, a);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((vmm_kernel<true, kOutSplitK>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((vmm_kernel<false, kOutSplitK>), grid, block, 0, s, a);
+  }
+  return check_launch(out_mode == kOutAccumulate ? "grinqh_decode_vmm_accumulate"
+                                                 : (fused ? "grinqh_decode_vmm" : "grinqh_vmm"));
 }
 
 int launch_vmm_list(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
@@ -267,7 +442,7 @@ int launch_vmm_list(const uint8_t* planes, const uint16_t* scales, const uint16_
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.bits = bits; a.active_idx = active_idx; a.n_active = n_active;
   a.y = y; a.K = K; a.N = N;
-  return launch_vmm(false, a, ws, s);
+  return launch_vmm(false, kOutSplitK, a, ws, s);
 }
 
 int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
@@ -276,7 +451,16 @@ int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.y = y; a.K = K; a.N = N; a.ap = ap;
-  return launch_vmm(true, a, ws, s);
+  return launch_vmm(true, kOutSplitK, a, ws, s);
+}
+
+int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                          const uint16_t* x, int64_t K, int64_t N, const AssignParams& ap, float* y,
+                          float* clear, hipStream_t s) {
+  VmmArgs a{};
+  a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
+  a.y = y; a.clear = clear; a.K = K; a.N = N; a.ap = ap;
+  return launch_vmm(true, kOutAccumulate, a, nullptr, s);
 }
 
 }  // namespace grinqh

@@ -161,6 +161,25 @@ int grinqh_decode_vmm(const uint8_t* planes, const uint16_t* scales, const uint1
                       const float* thresholds, const uint8_t* levels, int n, float* y,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Accumulating form of grinqh_decode_vmm: y[j] += (x W)[j] for the same
+ * decode-stage VMM (sections 3.1 and 3.3).  Workgroups add their results into
+ * y with fp32 device-scope atomic adds, so no split-K workspace and no final
+ * reduction pass are needed; the order of the additions is not fixed, so the
+ * last bits of y can differ from run to run.
+ * y:     fp32 [N], read and updated.  Zero it first for a plain product, or
+ *        pass the residual stream of a projection that adds into it.
+ * clear: fp32 [N] or NULL.  When given, this call sets it to zero, so a decode
+ *        loop can alternate two output buffers without a separate fill launch.
+ *        It must not overlap y.
+ * Other arguments as in grinqh_decode_vmm (no workspace).
+ * Errors: as grinqh_decode_vmm, and EINVAL when clear overlaps y.
+ */
+int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                                 const uint16_t* x, int64_t K, int64_t N,
+                                 const float* thresholds, const uint8_t* levels, int n,
+                                 float* y, float* clear, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for name in names:
         assert hasattr(lib, name), name
         assert name in g._SIGNATURES, name
@@ -96,6 +96,20 @@ def test_vmm_validation(lib):
     assert r == g.EINVAL
     r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 0, 4096, ctypes.cast(th, ctypes.c_void_p),
                               ctypes.cast(lv, ctypes.c_void_p), 1, FAKE, FAKE, need, None)
+    assert r == g.EINVAL
+
+
+def test_accumulate_validation(lib):
+    th = (ctypes.c_float * 1)(1.0)
+    lv = (ctypes.c_uint8 * 2)(0, 8)
+    thp, lvp = ctypes.cast(th, ctypes.c_void_p), ctypes.cast(lv, ctypes.c_void_p)
+    y = 0x100000
+    # clear overlapping y is rejected; clear == NULL is allowed (fails later only on bad args)
+    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, thp, lvp, 1, y, y + 128, None)
+    assert r == g.EINVAL and "overlap" in _err(lib)
+    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, thp, lvp, 1, None, None, None)
+    assert r == g.EINVAL
+    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, thp, lvp, -2, y, None, None)
     assert r == g.EINVAL
 
 

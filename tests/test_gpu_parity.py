@@ -250,3 +250,41 @@ def test_full_size_sampled_columns(K, N, cfg, mat, P, levels):
     r = np.random.default_rng(K + N)
     cols = np.unique(np.concatenate([r.choice(N, 192, replace=False), [0, 31, 32, 1023, 1024, N - 1]]))
     _check_y(y, lay.codes, lay.scales, lay.zeros, x, bits, cols)
+
+
+# ------------------------------------------------------ accumulating entry point
+
+@pytest.mark.parametrize("K,N,cfg,mat,P,levels", [CASES[0], CASES[2], CASES[4], CASES[5], CASES[7], CASES[8], CASES[9]])
+def test_decode_vmm_accumulate_parity(K, N, cfg, mat, P, levels):
+    lay = layer(K, N, cfg, mat)
+    th = oracle.calibrate(lay.calib, P)
+    x = lay.x[0]
+    planes = grq.pack(_dev(lay.codes))
+    y0 = np.random.default_rng(K + N).standard_normal(N).astype(np.float32)
+    y = _dev(y0.copy())
+    clear = torch.ones(N, dtype=torch.float32, device="cuda")
+    grq.decode_vmm_accumulate(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), K, N, th, levels, y, clear)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(clear).item() == 0
+    bits = oracle.assign(x, th, levels)
+    ref = oracle.vmm(lay.codes, lay.scales, lay.zeros, x, bits) + y0.astype(np.float64)
+    mag = oracle.vmm_abs(lay.codes, lay.scales, lay.zeros, x, bits) + np.abs(y0.astype(np.float64))
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= REL_TOL * mag + ABS_TOL)
+
+
+def test_decode_vmm_accumulate_ping_pong():
+    """Two buffers alternate: each call adds into one and clears the other."""
+    lay = layer(4096, 4096, 1, 0)
+    th = oracle.calibrate(lay.calib, synthetic.P_LEVELS_5[3])
+    planes = grq.pack(_dev(lay.codes))
+    sc, zr = _dev(lay.scales), _dev(lay.zeros)
+    bufs = [torch.zeros(4096, dtype=torch.float32, device="cuda") for _ in range(2)]
+    for step in range(3):
+        x = lay.x[step % 2]
+        grq.decode_vmm_accumulate(planes, sc, zr, _dev(x), 4096, 4096, th, synthetic.LEVELS_5,
+                                  bufs[step % 2], bufs[(step + 1) % 2])
+        torch.cuda.synchronize()
+        _check_y(bufs[step % 2].cpu().numpy(), lay.codes, lay.scales, lay.zeros, x,
+                 oracle.assign(x, th, synthetic.LEVELS_5))
+        assert torch.count_nonzero(bufs[(step + 1) % 2]).item() == 0
