@@ -71,7 +71,7 @@ using namespace grinqh;
 
 extern "C" {
 
-int grinqh_layout_version(void) { return 2; }
+int grinqh_layout_version(void) { return 3; }
 
 const char* grinqh_status_string(int status) {
   switch (status) {

@@ -16,6 +16,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(const uint16_t* 
                                                                 int32_t* __restrict__ active_idx,
                                                                 int32_t* __restrict__ n_active) {
   __shared__ int wave_tot[kAssignThreads / 64];
+  const AssignRegs ar = load_assign_regs(ap);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(const uint16_t* 
     for (int e = 0; e < kAssignPerThread; ++e) {
       const int64_t i = e0 + e;
       b[e] = 0;
-      if (i < K) b[e] = level_bits(level_of(x[i], ap), ap);
+      if (i < K) b[e] = bits_of(x[i], ar);
       cnt += b[e] > 0 ? 1 : 0;
     }
 #pragma unroll

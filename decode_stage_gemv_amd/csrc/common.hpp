@@ -16,11 +16,11 @@ constexpr int kMaxThresholds = GRINQH_MAX_THRESHOLDS;
 // Thresholds and levels travel as a kernel argument (a few SGPR loads).
 struct AssignParams {
   float th[kMaxThresholds];
-  uint8_t lv[kMaxThresholds + 1];
+  uint32_t lv[kMaxThresholds + 1];   // 32-bit so the kernel reads them with scalar loads
   int n;
 };
 
-__host__ __device__ inline int64_t padded_cols(int64_t N) { return (N + 31) / 32 * 32; }
+__host__ __device__ inline int64_t padded_cols(int64_t N) { return (N + 127) / 128 * 128; }
 __host__ __device__ inline int64_t n_tiles(int64_t N) { return (padded_cols(N) + kTile - 1) / kTile; }
 __host__ __device__ inline int64_t n_groups(int64_t K) { return (K + kGroup - 1) / kGroup; }
 
@@ -43,6 +43,34 @@ __device__ inline uint32_t level_bits(int k, const AssignParams& ap) {
   uint32_t b = ap.lv[0];
 #pragma unroll
   for (int t = 1; t <= kMaxThresholds; ++t) b = (k >= t) ? (uint32_t)ap.lv[t] : b;
+  return b;
+}
+
+// Thresholds and levels held in wave-uniform registers (read once per kernel).
+struct AssignRegs {
+  float th[kMaxThresholds];
+  uint32_t lv[kMaxThresholds + 1];
+  int n;
+};
+
+__device__ inline AssignRegs load_assign_regs(const AssignParams& ap) {
+  AssignRegs r;
+#pragma unroll
+  for (int t = 0; t < kMaxThresholds; ++t)
+    r.th[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, ap.th[t])));
+#pragma unroll
+  for (int t = 0; t <= kMaxThresholds; ++t) r.lv[t] = __builtin_amdgcn_readfirstlane(ap.lv[t]);
+  r.n = __builtin_amdgcn_readfirstlane(ap.n);
+  return r;
+}
+
+// b = levels[#thresholds reached]; with non-decreasing thresholds the reached
+// ones are a prefix, so the last one reached names the level.
+__device__ inline uint32_t bits_of(uint16_t xh, const AssignRegs& r) {
+  const float ax = __builtin_fabsf(half_bits_to_float(xh));
+  uint32_t b = r.lv[0];
+#pragma unroll
+  for (int t = 0; t < kMaxThresholds; ++t) b = (t < r.n && ax >= r.th[t]) ? r.lv[t + 1] : b;
   return b;
 }
 

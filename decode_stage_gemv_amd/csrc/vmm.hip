@@ -1,47 +1,65 @@
 // Decode-stage VMM over the bit-plane store (GRINQH paper, section 3.3
 // "Weight Reconstruction and Bias Correction"; Appendix C.1).
 //
-// Work split.  A workgroup owns one column tile (<= 1024 columns, one row
-// tile of the store per row) and one 128-row group of K, so every row it
-// touches shares one (scale, zero) row.  Its active rows are sorted by bit
-// width and taken two at a time; each 32-lane group of the workgroup owns a
-// stream of row pairs, and lane l of a group owns plane word l (32 columns).
+// Work split.  A workgroup owns one column tile (one row tile of the store
+// per row, ct <= 1024 columns) and one 128-row group of K, so every row it
+// touches shares one (scale, zero) row.
 //
-// Per row pair and lane: the b planes of each row are fetched with buffer
-// loads whose offset is pushed out of range for planes the row does not need
-// (they return 0 and move no data), so every iteration issues the same number
-// of loads and the next pair's loads are in flight while the current pair is
-// computed.  The codes come back from the planes through a bit-transpose
-// network specialised for b (bitplane.hpp); byte j of code word m from the two
-// rows is paired into one fp16x2 operand (the code as an fp16 subnormal,
-// c * 2^-24) and v_dot2 multiplies it by the pair's fp16 activations, adding
-// into an fp32 accumulator: one dot per two weights.  With the group factored
-// out,
+// Staging.  The group's active rows are sorted by bit width; row e gets b_e
+// consecutive "plane slots" (one slot = one plane of the row tile, ct / 8
+// bytes), so the workgroup's whole working set is sum_e b_e slots.  The slots
+// stream into a four-chunk LDS ring (128 slots per chunk) with direct-to-LDS
+// 16-byte buffer loads: lane L of a load instruction fetches one 16-byte piece
+// of one slot, found through a slot -> row table, so each instruction moves
+// 1 KB of needed bytes and nothing else.  Every wave issues the same number of
+// load instructions per chunk, so the loads of three chunks stay in flight
+// while the current one is computed.
+//
+// Compute.  Row pairs are formed from consecutive sorted rows; a 32-lane group
+// owns a pair, lane l owns 32 columns (one plane word).  The codes come back
+// from the planes through a bit-transpose network (bitplane.hpp); byte j of
+// code word m from the two rows is paired into one fp16x2 operand (the code as
+// an fp16 subnormal, c * 2^-24) and v_dot2 multiplies it by the pair's fp16
+// activations into an fp32 accumulator: one dot per two weights.  With the
+// group factored out,
 //   sum_i x_i (s r_ij + z) = s (A_j + H) + z X,
 //   A_j = sum_i x_i (q_ij with low 8-b_i bits cleared),
 //   H = sum_i x_i phi_i,  X = sum_i x_i,
-// so the scale and zero are applied once per column per workgroup.
+// so scale and zero are applied once per column per workgroup.
 //
-// Reduction across workgroups of a tile (split K): each workgroup writes one
-// partial row; the last to arrive (per-tile counter) adds them in split order
-// and writes y, so y does not depend on scheduling.
-#include <stdlib.h>
-
+// Output.  Split-K mode writes one partial row per workgroup; the last one to
+// arrive (per-tile counter) adds them in split order, so y does not depend on
+// scheduling.  Accumulate mode adds into y with fp32 device-scope atomics.
 #include "bitplane.hpp"
 #include "common.hpp"
 
 namespace grinqh {
 
-constexpr int kVmmThreads = 512;
-constexpr int kWaves = kVmmThreads / 64;
-constexpr int kLaneGroups = kVmmThreads / 32;
-constexpr int kRowsPerWG = kGroup;
-constexpr uint32_t kOutOfRange = 0x7FFFFF00u;   // buffer offset beyond any tile block
-constexpr uint32_t kRsrcWord3 = 0x00020000u;    // raw 32-bit buffer, gfx9 family
-
-constexpr int kScopeDevice = 16;              // cache-policy bits: sc1 = device scope
+constexpr int kVmmThreads = 512;                 // 8 waves
+constexpr int kLaneGroups = kVmmThreads / 32;    // 16 groups of 32 lanes
+constexpr int kRowsPerWG = kGroup;               // one scale group per workgroup
+constexpr int kChunkSlots = 128;                 // plane slots per staging chunk
+constexpr int kRingChunks = 4;
+constexpr int kRingSlots = kChunkSlots * kRingChunks;
+constexpr int kMaxSlots = kRowsPerWG * 8;
+constexpr int kMaxChunks = kMaxSlots / kChunkSlots;
+constexpr int kInstPerWave = 2;                  // 8 waves x 2 x 1 KB = one 128-slot chunk of 128-byte planes
+constexpr int kRingBytes = kRingSlots * 128;     // 64 KB
+constexpr int kTrashBytes = 1024;                // target of load slots a chunk does not need
+constexpr int kRedStride = 33;                   // LDS row stride of the lane-group reduction
+constexpr int kBigWords = kLaneGroups * 32 * kRedStride;   // reduction area; the ring + trash fit inside
+static_assert((kRingBytes + kTrashBytes) / 4 <= kBigWords, "ring must fit in the shared area");
+constexpr uint32_t kOutOfRange = 0x7FFFFF00u;    // buffer offset beyond any range used here
+constexpr uint32_t kRsrcWord3 = 0x00020000u;     // raw 32-bit buffer, gfx9 family
+constexpr int kScopeDevice = 16;                 // cache-policy bits: sc1 = device scope
+// s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]; all-ones fields mean "do not wait".
+constexpr int kWaitVm4 = 0x0F70 | (2 * kInstPerWave);   // vmcnt(4) only
+constexpr int kWaitVm0 = 0x0F70;                         // vmcnt(0) only
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 VmmGeometry vmm_geometry(int64_t K, int64_t N) {
   VmmGeometry g;
@@ -98,61 +116,77 @@ __device__ int64_t wave_lower_bound(const int32_t* __restrict__ idx, int64_t n, 
   return lo;
 }
 
-// One row pair's plane words and activations.
-struct PairRegs {
-  uint32_t w1[8], w2[8];
-  uint32_t xp;     // fp16 x of row 1 (low half) and row 2 (high half)
-  int b1, b2;
-};
-
-__device__ inline void issue_pair(__amdgpu_buffer_rsrc_t rsrc, int q, int npairs, int m,
-                                  const int* s_row, const int* s_bits, const uint16_t* s_xh,
-                                  int ct, uint32_t lane_off, bool lane_ok, PairRegs& r) {
-  int r1 = 0, r2 = 0, b1 = 0, b2 = 0;
-  uint32_t x1 = 0, x2 = 0;
-  if (q < npairs) {
-    const int e1 = 2 * q, e2 = 2 * q + 1;
-    r1 = s_row[e1];
-    b1 = s_bits[e1];
-    x1 = s_xh[e1];
-    if (e2 < m) {
-      r2 = s_row[e2];
-      b2 = s_bits[e2];
-      x2 = s_xh[e2];
-    }
-  }
-  if (!lane_ok) b1 = b2 = 0;
-  const uint32_t ps = (uint32_t)ct / 8;
-  const uint32_t base1 = (uint32_t)r1 * (uint32_t)ct + lane_off;
-  const uint32_t base2 = (uint32_t)r2 * (uint32_t)ct + lane_off;
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const uint32_t o1 = p < b1 ? base1 + (uint32_t)p * ps : kOutOfRange;
-    const uint32_t o2 = p < b2 ? base2 + (uint32_t)p * ps : kOutOfRange;
-    r.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)o1, 0, 0);
-    r.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)o2, 0, 0);
-  }
-  r.xp = x1 | (x2 << 16);
-  r.b1 = b1;
-  r.b2 = b2;
+// One 16-byte-per-lane direct-to-LDS buffer load: lane L's piece lands at
+// dst + 16 L (dst must be wave-uniform).  Written as inline asm so that the
+// compiler does not treat every later LDS read as dependent on it (it would
+// wait for all outstanding loads); the staging loop waits for exactly the
+// chunk it needs with s_waitcnt.  The instruction has no result register, and
+// its address register is read when it issues.
+__device__ inline void lds_load16(const u32x4& rsrc, void* dst, uint32_t voff) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)dst);
+  uint32_t saved_m0;
+  // M0 carries the LDS base; it is saved and restored around the load.
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc)
+      : "memory");
 }
 
-__device__ inline void compute_pair(const PairRegs& r, float (&acc)[32]) {
-  if ((r.b1 | r.b2) == 0) return;
-  uint32_t d1[8], d2[8];
-  planes_to_codes_rt(r.b1, r.w1, d1);
-  planes_to_codes_rt(r.b2, r.w2, d2);
-  const half2_t xv = __builtin_bit_cast(half2_t, r.xp);
+// phi * x for one row: the midpoint term of section 3.3 (0 at b = 8 and for no row).
+__device__ inline float phi_x(int b, float x) {
+  return (b > 0 && b < 8) ? x * __builtin_bit_cast(float, (uint32_t)(127 + 7 - b) << 23) : 0.0f;
+}
+
+// Rebuild two rows' codes.  The bit widths branch on scalar values when the
+// whole wave agrees (the usual case: rows are sorted by width) and fall back
+// to the full 8-plane network otherwise (planes a row does not have are 0).
+__device__ inline void rebuild_pair(int b1, int b2, const uint32_t (&w1)[8], const uint32_t (&w2)[8],
+                                    uint32_t (&d1)[8], uint32_t (&d2)[8]) {
+  const int u1 = __builtin_amdgcn_readfirstlane(b1);
+  const int u2 = __builtin_amdgcn_readfirstlane(b2);
+  if (__ballot(b1 != u1 || b2 != u2) == 0) {
+    planes_to_codes_rt(u1, w1, d1);
+    planes_to_codes_rt(u2, w2, d2);
+  } else {
+    planes_to_codes<8>(w1, d1);
+    planes_to_codes<8>(w2, d2);
+  }
+}
+
+// acc[4m + j] += x1 * row1 code + x2 * row2 code for the 32 columns of a lane:
+// bytes [row1 code, 0, row2 code, 0] form two fp16 subnormals c * 2^-24.
+__device__ inline void dot_pair(const uint32_t (&d1)[8], const uint32_t (&d2)[8], half2_t xv, float (&acc)[32]) {
 #pragma unroll
   for (int mm = 0; mm < 8; ++mm) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // bytes: [row1 code, 0, row2 code, 0] -> two fp16 subnormals c * 2^-24
-      const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t sel = (uint32_t)jj | (0x0Cu << 8) | ((uint32_t)(4 + jj) << 16) | (0x0Cu << 24);
       const uint32_t pr = __builtin_amdgcn_perm(d2[mm], d1[mm], sel);
-      acc[4 * mm + j] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr), xv, acc[4 * mm + j], false);
+      acc[4 * mm + jj] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr), xv, acc[4 * mm + jj], false);
     }
   }
+}
+
+// Both rows have B planes at 128-byte slots starting at r1 / r2 (this lane's
+// word already added): B LDS reads each with immediate offsets, then the
+// B-specialised rebuild.
+template <int B>
+__device__ inline void pair_fast(const uint8_t* r1, const uint8_t* r2, half2_t xv, float (&acc)[32]) {
+  uint32_t w1[8], w2[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    w1[p] = p < B ? *reinterpret_cast<const uint32_t*>(r1 + p * 128) : 0u;
+    w2[p] = p < B ? *reinterpret_cast<const uint32_t*>(r2 + p * 128) : 0u;
+  }
+  uint32_t d1[8], d2[8];
+  planes_to_codes<B>(w1, d1);
+  planes_to_codes<B>(w2, d2);
+  dot_pair(d1, d2, xv, acc);
 }
 
 // Output modes.
@@ -163,38 +197,52 @@ enum : int {
 
 template <bool kFused, int kOut>
 __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
-  __shared__ int s_row[kRowsPerWG];
-  __shared__ int s_bits[kRowsPerWG];
+  __shared__ __attribute__((aligned(16))) uint32_t s_big[kBigWords];   // staging ring | reduction
+  __shared__ uint32_t s_slot_off[kMaxSlots];  // plane slot -> byte offset of that plane in the group's row tiles
+  __shared__ int16_t s_row[kRowsPerWG];       // sorted row -> row within the group
+  __shared__ uint8_t s_b[kRowsPerWG];
   __shared__ uint16_t s_xh[kRowsPerWG];
+  __shared__ uint16_t s_slot0[kRowsPerWG];    // first plane slot of a sorted row
   __shared__ int s_cnt[2][9];
-  __shared__ int s_m;
-  __shared__ int s_p0;
-  __shared__ float s_hx[2][2];
-  __shared__ int s_last;
-  __shared__ float s_red[kLaneGroups * 32 * 33];
+  __shared__ int s_qs[kMaxChunks + 2];        // first pair of each chunk
+  __shared__ int s_m, s_p0, s_stot, s_last;
+  __shared__ float s_hx[kLaneGroups][2];
 
+  const AssignRegs ar = load_assign_regs(a.ap);   // scalar registers, read before any global load
   const int tile = blockIdx.x % a.tiles;
   const int split = blockIdx.x / a.tiles;
   const int64_t k0 = (int64_t)split * kRowsPerWG;
   const int64_t k1 = (k0 + kRowsPerWG) < a.K ? (k0 + kRowsPerWG) : a.K;
   const int64_t Np = padded_cols(a.N);
   const int64_t t0 = (int64_t)tile * kTile;
-  const int ct = (int)((Np - t0) < kTile ? (Np - t0) : kTile);
+  const int ct = (int)((Np - t0) < kTile ? (Np - t0) : kTile);   // multiple of 128
+  const int pb = ct / 8;                                          // bytes per plane slot, multiple of 16
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
-  const int64_t g = split;   // one 128-row group per workgroup
+  const int64_t g = split;
 
-  // ---- scale and zero of this thread's two output columns (tid, tid + 512),
-  // fetched now so their latency hides behind the rest of the work
-  uint16_t sc[2] = {0, 0}, zr[2] = {0, 0};
+  // ---- activation first, then scale and zero of this thread's two output
+  // columns (tid, tid + 512).  All loads are unconditional (clamped index,
+  // validity applied later) so nothing waits on them before it is needed.
+  uint32_t b = 0;
+  uint16_t xh = 0;
+  int rloc = 0;
+  uint16_t xr = 0;
+  if constexpr (kFused) {
+    // every thread loads (waves 2..7 repeat rows 0..127): no branch around the load
+    const int64_t i = k0 + (tid & (kRowsPerWG - 1));
+    xr = a.x[i < k1 ? i : k1 - 1];
+  }
+  uint16_t sc[2], zr[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int col = tid + u * kVmmThreads;
-    if (col < ct && t0 + col < a.N) {
-      sc[u] = a.scales[g * a.N + t0 + col];
-      zr[u] = a.zeros[g * a.N + t0 + col];
-    }
+    int col = tid + u * kVmmThreads;
+    col = col < ct ? col : ct - 1;
+    int64_t gc = t0 + col;
+    gc = gc < a.N ? gc : a.N - 1;
+    sc[u] = a.scales[g * a.N + gc];
+    zr[u] = a.zeros[g * a.N + gc];
   }
   if constexpr (kOut == kOutAccumulate) {
     // the caller's next output buffer, zeroed once per column (split 0 only)
@@ -207,8 +255,15 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
     }
   }
 
-  // ---- gather this group's candidate rows: thread t < 128 holds one
-  if constexpr (!kFused) {
+  if constexpr (kFused) {
+    if (wid < 2) {
+      rloc = tid;
+      if (k0 + tid < k1) {
+        xh = xr;
+        b = bits_of(xh, ar);
+      }
+    }
+  } else {
     if (wid == 0) {
       const int64_t n = *a.n_active;
       const int64_t p0 = wave_lower_bound(a.active_idx, n, k0);
@@ -221,31 +276,19 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
       }
     }
     __syncthreads();
-  }
-  uint32_t b = 0;
-  uint16_t xh = 0;
-  int rloc = 0;
-  if (wid < 2) {
-    if constexpr (kFused) {
-      rloc = tid;
-      if (k0 + tid < k1) {
-        xh = a.x[k0 + tid];
-        b = level_bits(level_of(xh, a.ap), a.ap);
-      }
-    } else {
-      if (tid < s_m) {
-        const int64_t i = a.active_idx[s_p0 + tid];
-        if (i >= k0 && i < k1) {   // a well-formed list always is
-          rloc = (int)(i - k0);
-          b = a.bits[i];
-          b = b > 8u ? 8u : b;
-          xh = a.x[i];
-        }
+    if (wid < 2 && tid < s_m) {
+      const int64_t i = a.active_idx[s_p0 + tid];
+      if (i >= k0 && i < k1) {   // a well-formed list always is
+        rloc = (int)(i - k0);
+        b = a.bits[i];
+        b = b > 8u ? 8u : b;
+        xh = a.x[i];
       }
     }
   }
 
-  // ---- stable counting sort of active rows by bit width (1..8)
+  // ---- stable counting sort of active rows by bit width (1..8); a row's
+  // plane slots follow from the bucket sizes, no scan needed
   uint64_t my_mask = 0;
   if (wid < 2) {
 #pragma unroll
@@ -254,74 +297,173 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
       if (lane == 0) s_cnt[wid][v] = __popcll(mv);
       if (b == (uint32_t)v) my_mask = mv;
     }
-    // H = sum x phi and X = sum x over active rows (fixed butterfly order)
-    const float xf = half_bits_to_float(xh);
-    float h = (b > 0 && b < 8) ? xf * (float)(1 << (7 - (b > 0 ? b : 1))) : 0.0f;
-    float xs = b > 0 ? xf : 0.0f;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      h += __shfl_xor(h, off, 64);
-      xs += __shfl_xor(xs, off, 64);
-    }
-    if (lane == 0) {
-      s_hx[wid][0] = h;
-      s_hx[wid][1] = xs;
-    }
   }
   __syncthreads();
   if (wid < 2 && b > 0) {
-    int pos = (wid == 1) ? s_cnt[0][b] : 0;
-    for (int v = 1; v < (int)b; ++v) pos += s_cnt[0][v] + s_cnt[1][v];
-    pos += __popcll(my_mask & ((1ull << lane) - 1ull));
-    s_row[pos] = rloc;
-    s_bits[pos] = (int)b;
+    int row_base = 0, slot_base = 0;
+#pragma unroll
+    for (int v = 1; v < 8; ++v) {
+      const int c = s_cnt[0][v] + s_cnt[1][v];
+      row_base += v < (int)b ? c : 0;
+      slot_base += v < (int)b ? v * c : 0;
+    }
+    const int rank = ((wid == 1) ? s_cnt[0][b] : 0) + __popcll(my_mask & ((1ull << lane) - 1ull));
+    const int pos = row_base + rank;
+    const int slot0 = slot_base + rank * (int)b;
+    s_row[pos] = (int16_t)rloc;
+    s_b[pos] = (uint8_t)b;
     s_xh[pos] = xh;
+    s_slot0[pos] = (uint16_t)slot0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      if (p < (int)b) s_slot_off[slot0 + p] = (uint32_t)rloc * (uint32_t)ct + (uint32_t)(p * pb);
   }
   if (tid == 0) {
-    int m = 0;
-    for (int v = 1; v <= 8; ++v) m += s_cnt[0][v] + s_cnt[1][v];
+    int m = 0, stot = 0;
+#pragma unroll
+    for (int v = 1; v <= 8; ++v) {
+      const int c = s_cnt[0][v] + s_cnt[1][v];
+      m += c;
+      stot += v * c;
+    }
     s_m = m;
+    s_stot = stot;
   }
   __syncthreads();
   const int m = s_m;
+  const int stot = s_stot;
+  const int npairs = (m + 1) / 2;
+  const int nchunks = (stot + kChunkSlots - 1) / kChunkSlots;
 
-  // ---- stream row pairs: lane group lg takes pairs lg, lg + 16, lg + 32,
-  // lg + 48 (at most 64 pairs per group), three in flight at a time
+  // ---- pair q is ready once the chunk holding its last slot has landed
+  if (wid == 0) {
+    int rc = kMaxChunks + 1;
+    if (lane < npairs) {
+      const int e = (2 * lane + 1 < m) ? 2 * lane + 1 : m - 1;
+      rc = ((int)s_slot0[e] + (int)s_b[e] - 1) / kChunkSlots;
+    }
+#pragma unroll
+    for (int c = 0; c <= kMaxChunks; ++c) {
+      const int n_before = __popcll(__ballot(rc < c));
+      if (lane == 0) s_qs[c] = n_before;
+    }
+  }
+
+  // ---- staging: each wave issues kInstPerWave 1 KB direct-to-LDS loads per chunk
+  // buffer descriptor over this group's row tiles (base, stride 0, size, format word)
+  u32x4 rsrc;
+  {
+    const uint64_t base = (uint64_t)(uintptr_t)(a.planes + t0 * a.K + k0 * ct);
+    rsrc.x = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    rsrc.y = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xFFFFu);
+    rsrc.z = __builtin_amdgcn_readfirstlane((uint32_t)((k1 - k0) * ct));
+    rsrc.w = kRsrcWord3;
+  }
+  uint8_t* const ring = reinterpret_cast<uint8_t*>(s_big);
+  uint8_t* const trash = ring + kRingBytes;
+  const int pps = pb / 16;                 // 16-byte pieces per slot (1..8)
+  // floor(n / pps) = (n * magic) >> 16 exactly for n < 8192, pps <= 8
+  const uint32_t pps_magic = (0x10000u + (uint32_t)pps - 1u) / (uint32_t)pps;
+  const int chunk_bytes = kChunkSlots * pb;
+  __syncthreads();   // s_qs, slot table, row tables visible
+
+  auto issue_chunk = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kInstPerWave; ++i) {
+      const int j = kInstPerWave * wid + i;               // instruction slot within the chunk
+      const bool inst_ok = c < nchunks && j * 1024 < chunk_bytes;
+      const int piece = j * 64 + lane;                    // 16-byte piece within the chunk
+      const int sl = (int)(((uint32_t)piece * pps_magic) >> 16);   // slot within the chunk
+      const int s = c * kChunkSlots + sl;                           // plane slot
+      const bool ok = inst_ok && s < stot;
+      const uint32_t off = ok ? s_slot_off[s] + (uint32_t)((piece - sl * pps) * 16) : kOutOfRange;
+      uint8_t* dst = inst_ok ? ring + (c % kRingChunks) * chunk_bytes + j * 1024 : trash;
+      lds_load16(rsrc, dst, off);
+    }
+  };
+
   const int lg = tid >> 5;
   const int ll = tid & 31;
   const bool lane_ok = ll < ct / 32;
-  // Descriptor over this group's row tiles only: row r of the group starts at r * ct.
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.planes + t0 * a.K + k0 * ct), (short)0, (int)((k1 - k0) * ct), (int)kRsrcWord3);
-  const uint32_t lane_off = 4u * (uint32_t)ll;
-  const int npairs = (m + 1) / 2;
   float acc[32];
 #pragma unroll
   for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
-  {
-    PairRegs p0, p1, p2;
-    issue_pair(rsrc, lg, npairs, m, s_row, s_bits, s_xh, ct, lane_off, lane_ok, p0);
-    issue_pair(rsrc, lg + kLaneGroups, npairs, m, s_row, s_bits, s_xh, ct, lane_off, lane_ok, p1);
-    issue_pair(rsrc, lg + 2 * kLaneGroups, npairs, m, s_row, s_bits, s_xh, ct, lane_off, lane_ok, p2);
-    compute_pair(p0, acc);
-    issue_pair(rsrc, lg + 3 * kLaneGroups, npairs, m, s_row, s_bits, s_xh, ct, lane_off, lane_ok, p0);
-    compute_pair(p1, acc);
-    compute_pair(p2, acc);
-    compute_pair(p0, acc);
+  float h_acc = 0.0f, x_acc = 0.0f;   // this lane group's share of H and X
+
+  const bool full_tile = ct == kTile;
+  issue_chunk(0);
+  issue_chunk(1);
+  issue_chunk(2);
+  for (int c = 0; c < nchunks; ++c) {
+    // this wave's loads of chunk c are done once at most two later chunks'
+    // loads are outstanding; the barrier makes that true for every wave
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    __syncthreads();
+    for (int q = s_qs[c] + lg; q < s_qs[c + 1]; q += kLaneGroups) {
+      const int e1 = 2 * q, e2 = 2 * q + 1;
+      const int b1 = s_b[e1];
+      const int b2 = e2 < m ? (int)s_b[e2] : 0;
+      const uint32_t x1h = s_xh[e1], x2h = e2 < m ? (uint32_t)s_xh[e2] : 0u;
+      const int sl1 = s_slot0[e1] % kRingSlots, sl2 = e2 < m ? (int)s_slot0[e2] % kRingSlots : 0;
+      const float x1 = half_bits_to_float((uint16_t)x1h), x2 = half_bits_to_float((uint16_t)x2h);
+      h_acc += phi_x(b1, x1) + phi_x(b2, x2);
+      x_acc += x1 + (b2 > 0 ? x2 : 0.0f);
+      const half2_t xv = __builtin_bit_cast(half2_t, x1h | (x2h << 16));
+      // Fast path: the whole wave has one width B for both rows, the tile is a
+      // full 1024 columns and neither row wraps around the ring end.
+      const int ub = __builtin_amdgcn_readfirstlane(b1);
+      const bool fast = __ballot(!(full_tile && b1 == ub && b2 == ub && sl1 + ub <= kRingSlots &&
+                                   sl2 + ub <= kRingSlots)) == 0;
+      if (fast) {
+        const uint8_t* r1 = ring + sl1 * 128 + 4 * ll;
+        const uint8_t* r2 = ring + sl2 * 128 + 4 * ll;
+        switch (ub) {
+          case 1: pair_fast<1>(r1, r2, xv, acc); break;
+          case 2: pair_fast<2>(r1, r2, xv, acc); break;
+          case 3: pair_fast<3>(r1, r2, xv, acc); break;
+          case 4: pair_fast<4>(r1, r2, xv, acc); break;
+          case 5: pair_fast<5>(r1, r2, xv, acc); break;
+          case 6: pair_fast<6>(r1, r2, xv, acc); break;
+          case 7: pair_fast<7>(r1, r2, xv, acc); break;
+          default: pair_fast<8>(r1, r2, xv, acc); break;
+        }
+      } else {
+        uint32_t w1[8], w2[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          w1[p] = (p < b1 && lane_ok) ? *reinterpret_cast<const uint32_t*>(ring + ((sl1 + p) % kRingSlots) * pb + 4 * ll) : 0u;
+          w2[p] = (p < b2 && lane_ok) ? *reinterpret_cast<const uint32_t*>(ring + ((sl2 + p) % kRingSlots) * pb + 4 * ll) : 0u;
+        }
+        uint32_t d1[8], d2[8];
+        rebuild_pair(b1, b2, w1, w2, d1, d2);
+        dot_pair(d1, d2, xv, acc);
+      }
+    }
+    __syncthreads();          // chunk c - 1 is no longer read: its ring place can be refilled
+    issue_chunk(c + 3);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // trailing (empty) loads landed before the LDS is reused
+  __syncthreads();
 
   // ---- reduce the 16 lane groups in LDS (row stride 33 keeps both the
-  // writes and the column-wise reads free of bank conflicts).  A half-wave
-  // swap (v_permlane32_swap) would halve this, but this toolchain drops one of
-  // the swap's two results, so it is not used.
+  // writes and the column-wise reads free of bank conflicts)
+  float* red = reinterpret_cast<float*>(s_big);
   {
-    float* dst = s_red + (lg * 32 + ll) * 33;
+    float* dst = red + (lg * 32 + ll) * kRedStride;
 #pragma unroll
     for (int c = 0; c < 32; ++c) dst[c] = acc[c];
+    if (ll == 0) {
+      s_hx[lg][0] = h_acc;
+      s_hx[lg][1] = x_acc;
+    }
   }
   __syncthreads();
-  const float H = s_hx[0][0] + s_hx[1][0];
-  const float X = s_hx[0][1] + s_hx[1][1];
+  float H = 0.0f, X = 0.0f;
+#pragma unroll
+  for (int h = 0; h < kLaneGroups; ++h) {
+    H += s_hx[h][0];
+    X += s_hx[h][1];
+  }
   float val[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -329,7 +471,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
     if (m > 0 && col < ct && t0 + col < a.N) {
       float A = 0.0f;
 #pragma unroll
-      for (int h = 0; h < kLaneGroups; ++h) A += s_red[(h * 32 + (col >> 5)) * 33 + (col & 31)];
+      for (int h = 0; h < kLaneGroups; ++h) A += red[(h * 32 + (col >> 5)) * kRedStride + (col & 31)];
       A *= 16777216.0f;   // codes entered as c * 2^-24
       val[u] = half_bits_to_float(sc[u]) * (A + H) + half_bits_to_float(zr[u]) * X;
     }

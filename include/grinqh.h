@@ -25,8 +25,8 @@
  *   on one stream, or give each stream its own workspace).
  *
  * Store layout (this library's concrete form of the paper's bit-planar
- * store; grinqh_layout_version() == 2):
- * - N_pad = N rounded up to a multiple of 32.  Columns are cut into tiles of
+ * store; grinqh_layout_version() == 3):
+ * - N_pad = N rounded up to a multiple of 128.  Columns are cut into tiles of
  *   GRINQH_TILE = 1024 columns; tile t has width C_t = min(1024, N_pad - 1024 t).
  * - Tile t occupies bytes [1024 K t, 1024 K t + K C_t).  Inside it, row tile
  *   (t, i) starts at 1024 K t + i C_t and holds planes 0..7 back to back,
@@ -61,7 +61,7 @@ enum {
 #define GRINQH_MAX_THRESHOLDS 8   /* n <= 8 thresholds, n + 1 <= 9 levels */
 #define GRINQH_MAX_BITS 8         /* b_max */
 
-/* Version of the store layout described above (2). */
+/* Version of the store layout described above (3). */
 int grinqh_layout_version(void);
 
 /* Static description of a status code.  Never NULL. */

@@ -4,7 +4,7 @@ Only the tests, the smoke check and the CPU-baseline leg of bench.py may
 import this package; the HIP library never does.
 """
 from .grinqh_oracle import (  # noqa: F401
-    B_MAX, GROUP, TILE, WORD,
+    B_MAX, GROUP, TILE, WORD, PAD,
     cut_points, empirical_quantile, calibrate,
     assign, compact,
     padded_cols, tiles, planes_bytes, plane_offset, pack, read_planes, span_bytes,

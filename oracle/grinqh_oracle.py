@@ -29,6 +29,7 @@ GROUP = 128
 # first, the top b planes of one row one contiguous span.
 TILE = 1024          # output columns per row tile
 WORD = 32            # columns per 32-bit plane word
+PAD = 128            # N is padded to a multiple of this many columns
 
 
 # --------------------------------------------------------------------------
@@ -142,11 +143,11 @@ def compact(bits: np.ndarray):
 # --------------------------------------------------------------------------
 
 def padded_cols(N: int) -> int:
-    return ((N + WORD - 1) // WORD) * WORD
+    return ((N + PAD - 1) // PAD) * PAD
 
 
 def tiles(N: int):
-    """(start column, width) of each row tile; widths are multiples of 32."""
+    """(start column, width) of each row tile; widths are multiples of 128."""
     Np = padded_cols(N)
     return [(t0, min(TILE, Np - t0)) for t0 in range(0, Np, TILE)]
 

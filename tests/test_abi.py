@@ -34,12 +34,12 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_static_queries(lib):
-    assert lib.grinqh_layout_version() == 2
+    assert lib.grinqh_layout_version() == 3
     assert lib.grinqh_status_string(0) == b"ok"
     assert lib.grinqh_status_string(-1) == b"invalid argument"
     assert lib.grinqh_status_string(-2) == b"device error"
     assert lib.grinqh_planes_bytes(4096, 14336) == 4096 * 14336
-    assert lib.grinqh_planes_bytes(3, 33) == 3 * 64
+    assert lib.grinqh_planes_bytes(3, 33) == 3 * 128
     assert lib.grinqh_planes_bytes(0, 5) == -1
     assert lib.grinqh_workspace_bytes(-1, 5) == -1
     assert lib.grinqh_workspace_bytes(128, 4096) >= 0

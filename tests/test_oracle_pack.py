@@ -16,7 +16,7 @@ def _slow_pack(codes):
     words little-endian.
     """
     K, N = codes.shape
-    Np = -(-N // 32) * 32
+    Np = -(-N // 128) * 128
     out = bytearray(K * Np)
     t0 = 0
     t = 0
@@ -97,7 +97,8 @@ def test_read_touches_only_the_span():
 
 def test_store_size_and_offsets():
     assert oracle.planes_bytes(4096, 14336) == 4096 * 14336
-    assert oracle.planes_bytes(3, 33) == 3 * 64
-    assert [ct for _, ct in oracle.tiles(2100)] == [1024, 1024, 64]
+    assert oracle.planes_bytes(3, 33) == 3 * 128
+    assert [ct for _, ct in oracle.tiles(2100)] == [1024, 1024, 128]
+    assert [ct for _, ct in oracle.tiles(1400)] == [1024, 384]
     K = 10
-    assert oracle.plane_offset(K, 2100, 2, 3, 5) == 2 * K * 1024 + 3 * 64 + 5 * 8
+    assert oracle.plane_offset(K, 2100, 2, 3, 5) == 2 * K * 1024 + 3 * 128 + 5 * 16
