@@ -30,6 +30,43 @@ __host__ __device__ inline void swap_blocks(uint32_t& lo, uint32_t& hi) {
   hi = nhi;
 }
 
+// (a & m) | (b & ~m) as one v_bfi_b32 on the device.
+__host__ __device__ inline uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(m), "v"(a), "v"(b));
+  return r;
+#else
+  return (a & m) | (b & ~m);
+#endif
+}
+
+// swap_blocks when one side is known to be zero at compile time (LZ: lo is
+// zero, HZ: hi is zero); the full case is one shift and one bit select per
+// output.
+template <int k, uint32_t M, bool LZ, bool HZ>
+__host__ __device__ inline void swap_blocks_z(uint32_t& lo, uint32_t& hi) {
+  if constexpr (LZ && HZ) {
+  } else if constexpr (LZ) {
+    lo = (hi << k) & ~M;
+    hi = hi & ~M;
+  } else if constexpr (HZ) {
+    hi = (lo >> k) & M;
+    lo = lo & M;
+  } else {
+    const uint32_t nlo = bit_select(M, lo, hi << k);
+    hi = bit_select(M, lo >> k, hi);
+    lo = nlo;
+  }
+}
+
+// Which of v[0..7] are still zero after each stage, for B planes.
+__host__ __device__ constexpr bool zero0(int B, int r) { return 7 - r >= B; }
+__host__ __device__ constexpr bool zero1(int B, int r) { return zero0(B, r & 3) && zero0(B, (r & 3) + 4); }
+__host__ __device__ constexpr bool zero2(int B, int r) {
+  return zero1(B, r & 5) && zero1(B, (r & 5) + 2);
+}
+
 template <int B>
 __host__ __device__ inline void planes_to_codes(const uint32_t (&w)[8], uint32_t (&d)[8]) {
   // v[r] = plane 7 - r, so that after the transpose bit r of a code byte is
@@ -37,15 +74,31 @@ __host__ __device__ inline void planes_to_codes(const uint32_t (&w)[8], uint32_t
   uint32_t v[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) v[r] = (7 - r < B) ? w[7 - r] : 0u;
+  if constexpr (B <= 2) {
+    // few planes: plain shifts and masks, which the compiler folds well
 #pragma unroll
-  for (int r = 0; r < 4; ++r) swap_blocks<4, 0x0F0F0F0Fu>(v[r], v[r + 4]);
+    for (int r = 0; r < 4; ++r) swap_blocks<4, 0x0F0F0F0Fu>(v[r], v[r + 4]);
 #pragma unroll
-  for (int r = 0; r < 8; r += 4) {
-    swap_blocks<2, 0x33333333u>(v[r], v[r + 2]);
-    swap_blocks<2, 0x33333333u>(v[r + 1], v[r + 3]);
+    for (int r = 0; r < 8; r += 4) {
+      swap_blocks<2, 0x33333333u>(v[r], v[r + 2]);
+      swap_blocks<2, 0x33333333u>(v[r + 1], v[r + 3]);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; r += 2) swap_blocks<1, 0x55555555u>(v[r], v[r + 1]);
+  } else {
+    swap_blocks_z<4, 0x0F0F0F0Fu, zero0(B, 0), zero0(B, 4)>(v[0], v[4]);
+    swap_blocks_z<4, 0x0F0F0F0Fu, zero0(B, 1), zero0(B, 5)>(v[1], v[5]);
+    swap_blocks_z<4, 0x0F0F0F0Fu, zero0(B, 2), zero0(B, 6)>(v[2], v[6]);
+    swap_blocks_z<4, 0x0F0F0F0Fu, zero0(B, 3), zero0(B, 7)>(v[3], v[7]);
+    swap_blocks_z<2, 0x33333333u, zero1(B, 0), zero1(B, 2)>(v[0], v[2]);
+    swap_blocks_z<2, 0x33333333u, zero1(B, 1), zero1(B, 3)>(v[1], v[3]);
+    swap_blocks_z<2, 0x33333333u, zero1(B, 4), zero1(B, 6)>(v[4], v[6]);
+    swap_blocks_z<2, 0x33333333u, zero1(B, 5), zero1(B, 7)>(v[5], v[7]);
+    swap_blocks_z<1, 0x55555555u, zero2(B, 0), zero2(B, 1)>(v[0], v[1]);
+    swap_blocks_z<1, 0x55555555u, zero2(B, 2), zero2(B, 3)>(v[2], v[3]);
+    swap_blocks_z<1, 0x55555555u, zero2(B, 4), zero2(B, 5)>(v[4], v[5]);
+    swap_blocks_z<1, 0x55555555u, zero2(B, 6), zero2(B, 7)>(v[6], v[7]);
   }
-#pragma unroll
-  for (int r = 0; r < 8; r += 2) swap_blocks<1, 0x55555555u>(v[r], v[r + 1]);
 #pragma unroll
   for (int m = 0; m < 8; ++m) d[m] = v[m];
 }

@@ -5,27 +5,32 @@
 // per row, ct <= 1024 columns) and one 128-row group of K, so every row it
 // touches shares one (scale, zero) row.
 //
-// Staging.  The group's active rows are sorted by bit width; row e gets b_e
-// consecutive "plane slots" (one slot = one plane of the row tile, ct / 8
-// bytes), so the workgroup's whole working set is sum_e b_e slots.  The slots
-// stream into a four-chunk LDS ring (128 slots per chunk) with direct-to-LDS
-// 16-byte buffer loads: lane L of a load instruction fetches one 16-byte piece
-// of one slot, found through a slot -> row table, so each instruction moves
-// 1 KB of needed bytes and nothing else.  Every wave issues the same number of
-// load instructions per chunk, so the loads of three chunks stay in flight
-// while the current one is computed.
+// Row order.  Every wave sees all rows of the group (two per lane) and
+// buckets the active ones by bit width b with ballots, in registers.  Each
+// bucket is cut into "couples" of four rows of one width (the last couple of
+// a bucket is padded with empty rows: x = 0, no bytes).  A couple is two row
+// pairs; the two 32-lane halves of a wave take one pair each, lane l owning
+// 32 columns (one plane word of each row), so the bit width is the same for
+// the whole wave.  Couple k belongs to wave k mod 8 (its "records", in
+// order).
 //
-// Compute.  Row pairs are formed from consecutive sorted rows; a 32-lane group
-// owns a pair, lane l owns 32 columns (one plane word).  The codes come back
-// from the planes through a bit-transpose network (bitplane.hpp); byte j of
-// code word m from the two rows is paired into one fp16x2 operand (the code as
-// an fp16 subnormal, c * 2^-24) and v_dot2 multiplies it by the pair's fp16
-// activations into an fp32 accumulator: one dot per two weights.  With the
-// group factored out,
+// Loads.  A lane loads its pair's plane words straight into registers with
+// 4-byte buffer loads: planes p < b come from the row tile, planes p >= b use
+// an out-of-range scalar offset, which returns 0 and moves no bytes, so only
+// the top b planes of a row are fetched.  Two records are in flight per
+// wave (double buffer); a wave waits only for its own loads and never for
+// another wave until the final reduction.
+//
+// Compute.  The codes come back from the planes through a bit-transpose
+// network (bitplane.hpp); byte j of code word m from the two rows of a pair
+// is paired into one fp16x2 operand (the code as an fp16 subnormal,
+// c * 2^-24) and v_dot2 multiplies it by the pair's fp16 activations into an
+// fp32 accumulator: one dot per two weights.  With the group factored out,
 //   sum_i x_i (s r_ij + z) = s (A_j + H) + z X,
 //   A_j = sum_i x_i (q_ij with low 8-b_i bits cleared),
 //   H = sum_i x_i phi_i,  X = sum_i x_i,
-// so scale and zero are applied once per column per workgroup.
+// so scale and zero are applied once per column per workgroup, and H and X
+// are plain sums over the group's active rows.
 //
 // Output.  Split-K mode writes one partial row per workgroup; the last one to
 // arrive (per-tile counter) adds them in split order, so y does not depend on
@@ -36,30 +41,21 @@
 namespace grinqh {
 
 constexpr int kVmmThreads = 512;                 // 8 waves
-constexpr int kLaneGroups = kVmmThreads / 32;    // 16 groups of 32 lanes
+constexpr int kWaves = kVmmThreads / 64;
 constexpr int kRowsPerWG = kGroup;               // one scale group per workgroup
-constexpr int kChunkSlots = 128;                 // plane slots per staging chunk
-constexpr int kRingChunks = 4;
-constexpr int kRingSlots = kChunkSlots * kRingChunks;
-constexpr int kMaxSlots = kRowsPerWG * 8;
-constexpr int kMaxChunks = kMaxSlots / kChunkSlots;
-constexpr int kInstPerWave = 2;                  // 8 waves x 2 x 1 KB = one 128-slot chunk of 128-byte planes
-constexpr int kRingBytes = kRingSlots * 128;     // 64 KB
-constexpr int kTrashBytes = 1024;                // target of load slots a chunk does not need
-constexpr int kRedStride = 33;                   // LDS row stride of the lane-group reduction
-constexpr int kBigWords = kLaneGroups * 32 * kRedStride;   // reduction area; the ring + trash fit inside
-static_assert((kRingBytes + kTrashBytes) / 4 <= kBigWords, "ring must fit in the shared area");
+constexpr int kMaxCouples = kRowsPerWG / 4 + 6;  // sum over 8 widths of ceil(c_v / 4) <= (128 + 8 * 3) / 4
+constexpr int kMaxRecords = (kMaxCouples + kWaves - 1) / kWaves;
+constexpr int kRedStride = 33;                   // LDS row stride of the wave reduction
+constexpr int kRedWords = kWaves * 32 * kRedStride;
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;    // buffer offset beyond any range used here
-constexpr uint32_t kRsrcWord3 = 0x00020000u;     // raw 32-bit buffer, gfx9 family
+constexpr int kRsrcWord3 = 0x00020000;           // raw 32-bit buffer, gfx9 family
 constexpr int kScopeDevice = 16;                 // cache-policy bits: sc1 = device scope
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14],
 // expcnt [6:4], lgkmcnt [11:8]; all-ones fields mean "do not wait".
-constexpr int kWaitVm4 = 0x0F70 | (2 * kInstPerWave);   // vmcnt(4) only
-constexpr int kWaitVm0 = 0x0F70;                         // vmcnt(0) only
+constexpr int kWaitVm0 = 0x0F70;                 // vmcnt(0) only
+constexpr int kWaitVm16 = 0x4F70;                // vmcnt(16) only: one record's loads may be outstanding
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 VmmGeometry vmm_geometry(int64_t K, int64_t N) {
   VmmGeometry g;
@@ -116,46 +112,9 @@ __device__ int64_t wave_lower_bound(const int32_t* __restrict__ idx, int64_t n, 
   return lo;
 }
 
-// One 16-byte-per-lane direct-to-LDS buffer load: lane L's piece lands at
-// dst + 16 L (dst must be wave-uniform).  Written as inline asm so that the
-// compiler does not treat every later LDS read as dependent on it (it would
-// wait for all outstanding loads); the staging loop waits for exactly the
-// chunk it needs with s_waitcnt.  The instruction has no result register, and
-// its address register is read when it issues.
-__device__ inline void lds_load16(const u32x4& rsrc, void* dst, uint32_t voff) {
-  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)dst);
-  uint32_t saved_m0;
-  // M0 carries the LDS base; it is saved and restored around the load.
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved_m0)
-      : "s"(lds_addr), "v"(voff), "s"(rsrc)
-      : "memory");
-}
-
 // phi * x for one row: the midpoint term of section 3.3 (0 at b = 8 and for no row).
 __device__ inline float phi_x(int b, float x) {
   return (b > 0 && b < 8) ? x * __builtin_bit_cast(float, (uint32_t)(127 + 7 - b) << 23) : 0.0f;
-}
-
-// Rebuild two rows' codes.  The bit widths branch on scalar values when the
-// whole wave agrees (the usual case: rows are sorted by width) and fall back
-// to the full 8-plane network otherwise (planes a row does not have are 0).
-__device__ inline void rebuild_pair(int b1, int b2, const uint32_t (&w1)[8], const uint32_t (&w2)[8],
-                                    uint32_t (&d1)[8], uint32_t (&d2)[8]) {
-  const int u1 = __builtin_amdgcn_readfirstlane(b1);
-  const int u2 = __builtin_amdgcn_readfirstlane(b2);
-  if (__ballot(b1 != u1 || b2 != u2) == 0) {
-    planes_to_codes_rt(u1, w1, d1);
-    planes_to_codes_rt(u2, w2, d2);
-  } else {
-    planes_to_codes<8>(w1, d1);
-    planes_to_codes<8>(w2, d2);
-  }
 }
 
 // acc[4m + j] += x1 * row1 code + x2 * row2 code for the 32 columns of a lane:
@@ -172,21 +131,51 @@ __device__ inline void dot_pair(const uint32_t (&d1)[8], const uint32_t (&d2)[8]
   }
 }
 
-// Both rows have B planes at 128-byte slots starting at r1 / r2 (this lane's
-// word already added): B LDS reads each with immediate offsets, then the
-// B-specialised rebuild.
-template <int B>
-__device__ inline void pair_fast(const uint8_t* r1, const uint8_t* r2, half2_t xv, float (&acc)[32]) {
+// One record in flight: the lane's plane words of its pair (planes the rows
+// do not have are 0) and the pair's activations.
+struct RecordRegs {
   uint32_t w1[8], w2[8];
+  uint32_t xw;
+};
+
+// Issue the 16 loads of record j of this wave (width b; b = 0 for a record
+// the wave does not have) into r.  The record's row sources (byte offsets of
+// the row tiles within the group's block, out of range for padding rows) and
+// x pairs come from the wave's LDS tables.  Lane l of a pair loads plane word
+// l of planes p < b of both rows (plane p at scalar offset p pb from the row
+// tile); planes p >= b get an out-of-range voffset, which returns 0 and moves
+// no bytes.  Only the voffset takes part in the range check, so it alone
+// carries the out-of-range value.  Every call issues exactly 16 loads, so the
+// wait counts of the pipeline are the same on every path.
+__device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, const uint32_t* src,
+                                   const uint32_t* cx, int j, int b, int pb) {
+  const int h = (threadIdx.x >> 5) & 1;
+  const int ll = threadIdx.x & 31;
+  const int jj = j < kMaxRecords ? j : kMaxRecords - 1;   // table index (unused when b = 0)
+  const uint32_t s1 = b > 0 ? src[4 * jj + 2 * h] : kOutOfRange;
+  const uint32_t s2 = b > 0 ? src[4 * jj + 2 * h + 1] : kOutOfRange;
+  r.xw = b > 0 ? cx[2 * jj + h] : 0u;
+  const uint32_t v1 = s1 == kOutOfRange ? kOutOfRange : s1 + 4u * (uint32_t)ll;
+  const uint32_t v2 = s2 == kOutOfRange ? kOutOfRange : s2 + 4u * (uint32_t)ll;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    w1[p] = p < B ? *reinterpret_cast<const uint32_t*>(r1 + p * 128) : 0u;
-    w2[p] = p < B ? *reinterpret_cast<const uint32_t*>(r2 + p * 128) : 0u;
-  }
+  for (int p = 0; p < 8; ++p)
+    r.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(p < b ? v1 : kOutOfRange), p * pb, 0);
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+    r.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(p < b ? v2 : kOutOfRange), p * pb, 0);
+}
+
+// Rebuild and accumulate one record (width b, wave-uniform).
+__device__ inline void compute_record(const RecordRegs& r, int b, float (&acc)[32]) {
   uint32_t d1[8], d2[8];
-  planes_to_codes<B>(w1, d1);
-  planes_to_codes<B>(w2, d2);
-  dot_pair(d1, d2, xv, acc);
+  if (b <= 2) {
+    planes_to_codes<2>(r.w1, d1);   // planes past b are 0 already
+    planes_to_codes<2>(r.w2, d2);
+  } else {
+    planes_to_codes<8>(r.w1, d1);
+    planes_to_codes<8>(r.w2, d2);
+  }
+  dot_pair(d1, d2, __builtin_bit_cast(half2_t, r.xw), acc);
 }
 
 // Output modes.
@@ -197,16 +186,11 @@ enum : int {
 
 template <bool kFused, int kOut>
 __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_big[kBigWords];   // staging ring | reduction
-  __shared__ uint32_t s_slot_off[kMaxSlots];  // plane slot -> byte offset of that plane in the group's row tiles
-  __shared__ int16_t s_row[kRowsPerWG];       // sorted row -> row within the group
-  __shared__ uint8_t s_b[kRowsPerWG];
-  __shared__ uint16_t s_xh[kRowsPerWG];
-  __shared__ uint16_t s_slot0[kRowsPerWG];    // first plane slot of a sorted row
-  __shared__ int s_cnt[2][9];
-  __shared__ int s_qs[kMaxChunks + 2];        // first pair of each chunk
-  __shared__ int s_m, s_p0, s_stot, s_last;
-  __shared__ float s_hx[kLaneGroups][2];
+  __shared__ float s_red[kRedWords];                      // wave reduction
+  __shared__ uint32_t s_src[kWaves][kMaxRecords * 4];     // per wave: record row -> source byte offset
+  __shared__ uint32_t s_cx[kWaves][kMaxRecords * 2];      // per wave: record pair -> fp16 x of its rows
+  __shared__ float s_hx[2];
+  __shared__ int s_last;
 
   const AssignRegs ar = load_assign_regs(a.ap);   // scalar registers, read before any global load
   const int tile = blockIdx.x % a.tiles;
@@ -216,23 +200,26 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
   const int64_t Np = padded_cols(a.N);
   const int64_t t0 = (int64_t)tile * kTile;
   const int ct = (int)((Np - t0) < kTile ? (Np - t0) : kTile);   // multiple of 128
-  const int pb = ct / 8;                                          // bytes per plane slot, multiple of 16
+  const int pb = ct / 8;                                          // bytes per plane, multiple of 16
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int64_t g = split;
 
-  // ---- activation first, then scale and zero of this thread's two output
-  // columns (tid, tid + 512).  All loads are unconditional (clamped index,
-  // validity applied later) so nothing waits on them before it is needed.
-  uint32_t b = 0;
-  uint16_t xh = 0;
-  int rloc = 0;
-  uint16_t xr = 0;
+  // ---- every wave sees all rows of the group, two per lane (lane and lane
+  // + 64): activation loads first, then scale and zero of this thread's two
+  // output columns (tid, tid + 512).  Loads are unconditional (clamped
+  // index, validity applied later) so nothing waits on them early.
+  uint32_t bq[2] = {0u, 0u};   // bit width of the lane's two rows
+  uint16_t xq[2] = {0, 0};     // their fp16 activations
+  int rq[2] = {0, 0};          // their rows within the group
   if constexpr (kFused) {
-    // every thread loads (waves 2..7 repeat rows 0..127): no branch around the load
-    const int64_t i = k0 + (tid & (kRowsPerWG - 1));
-    xr = a.x[i < k1 ? i : k1 - 1];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int64_t i = k0 + lane + 64 * e;
+      xq[e] = a.x[i < k1 ? i : k1 - 1];
+      rq[e] = lane + 64 * e;
+    }
   }
   uint16_t sc[2], zr[2];
 #pragma unroll
@@ -256,14 +243,12 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
   }
 
   if constexpr (kFused) {
-    if (wid < 2) {
-      rloc = tid;
-      if (k0 + tid < k1) {
-        xh = xr;
-        b = bits_of(xh, ar);
-      }
-    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if (k0 + rq[e] < k1) bq[e] = bits_of(xq[e], ar);
   } else {
+    // the listed rows of this group: positions [p0, p0 + m) of the list
+    __shared__ int s_m, s_p0;
     if (wid == 0) {
       const int64_t n = *a.n_active;
       const int64_t p0 = wave_lower_bound(a.active_idx, n, k0);
@@ -276,194 +261,155 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
       }
     }
     __syncthreads();
-    if (wid < 2 && tid < s_m) {
-      const int64_t i = a.active_idx[s_p0 + tid];
-      if (i >= k0 && i < k1) {   // a well-formed list always is
-        rloc = (int)(i - k0);
-        b = a.bits[i];
-        b = b > 8u ? 8u : b;
-        xh = a.x[i];
+    const int m = s_m, p0 = s_p0;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int q = lane + 64 * e;
+      if (q < m) {
+        const int64_t i = a.active_idx[p0 + q];
+        if (i >= k0 && i < k1) {   // a well-formed list always is
+          rq[e] = (int)(i - k0);
+          uint32_t bb = a.bits[i];
+          bq[e] = bb > 8u ? 8u : bb;
+          xq[e] = a.x[i];
+        }
       }
     }
   }
 
-  // ---- stable counting sort of active rows by bit width (1..8); a row's
-  // plane slots follow from the bucket sizes, no scan needed
-  uint64_t my_mask = 0;
-  if (wid < 2) {
+  // ---- bucket the rows by width with ballots (every wave, no LDS): rows of
+  // width v, in lane order (first set, then second set), get ranks 0, 1, ...;
+  // rank r of width v -> couple cb_v + r / 4, place r % 4
+  int cnt[9];
+  uint64_t msk[2][9];
 #pragma unroll
-    for (int v = 1; v <= 8; ++v) {
-      const uint64_t mv = __ballot(b == (uint32_t)v);
-      if (lane == 0) s_cnt[wid][v] = __popcll(mv);
-      if (b == (uint32_t)v) my_mask = mv;
-    }
+  for (int v = 1; v <= 8; ++v) {
+    msk[0][v] = __ballot(bq[0] == (uint32_t)v);
+    msk[1][v] = __ballot(bq[1] == (uint32_t)v);
+    cnt[v] = __popcll(msk[0][v]) + __popcll(msk[1][v]);
   }
-  __syncthreads();
-  if (wid < 2 && b > 0) {
-    int row_base = 0, slot_base = 0;
+  int cbv[10];   // first couple of each width; cbv[9] = number of couples
+  cbv[0] = 0;
+  cbv[1] = 0;
 #pragma unroll
-    for (int v = 1; v < 8; ++v) {
-      const int c = s_cnt[0][v] + s_cnt[1][v];
-      row_base += v < (int)b ? c : 0;
-      slot_base += v < (int)b ? v * c : 0;
-    }
-    const int rank = ((wid == 1) ? s_cnt[0][b] : 0) + __popcll(my_mask & ((1ull << lane) - 1ull));
-    const int pos = row_base + rank;
-    const int slot0 = slot_base + rank * (int)b;
-    s_row[pos] = (int16_t)rloc;
-    s_b[pos] = (uint8_t)b;
-    s_xh[pos] = xh;
-    s_slot0[pos] = (uint16_t)slot0;
-#pragma unroll
-    for (int p = 0; p < 8; ++p)
-      if (p < (int)b) s_slot_off[slot0 + p] = (uint32_t)rloc * (uint32_t)ct + (uint32_t)(p * pb);
-  }
-  if (tid == 0) {
-    int m = 0, stot = 0;
-#pragma unroll
-    for (int v = 1; v <= 8; ++v) {
-      const int c = s_cnt[0][v] + s_cnt[1][v];
-      m += c;
-      stot += v * c;
-    }
-    s_m = m;
-    s_stot = stot;
-  }
-  __syncthreads();
-  const int m = s_m;
-  const int stot = s_stot;
-  const int npairs = (m + 1) / 2;
-  const int nchunks = (stot + kChunkSlots - 1) / kChunkSlots;
+  for (int v = 1; v <= 8; ++v) cbv[v + 1] = cbv[v] + ((cnt[v] + 3) >> 2);
+  const int ncp = cbv[9];
+  const int nrec = ncp > wid ? (ncp - wid + kWaves - 1) / kWaves : 0;   // this wave's couples
 
-  // ---- pair q is ready once the chunk holding its last slot has landed
   if (wid == 0) {
-    int rc = kMaxChunks + 1;
-    if (lane < npairs) {
-      const int e = (2 * lane + 1 < m) ? 2 * lane + 1 : m - 1;
-      rc = ((int)s_slot0[e] + (int)s_b[e] - 1) / kChunkSlots;
+    // H = sum x phi and X = sum x over the group's active rows
+    float hs = 0.0f, xs = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float xf = bq[e] > 0 ? half_bits_to_float(xq[e]) : 0.0f;
+      hs += phi_x((int)bq[e], xf);
+      xs += xf;
     }
 #pragma unroll
-    for (int c = 0; c <= kMaxChunks; ++c) {
-      const int n_before = __popcll(__ballot(rc < c));
-      if (lane == 0) s_qs[c] = n_before;
+    for (int off = 32; off >= 1; off >>= 1) {
+      hs += __shfl_xor(hs, off, 64);
+      xs += __shfl_xor(xs, off, 64);
+    }
+    if (lane == 0) {
+      s_hx[0] = hs;
+      s_hx[1] = xs;
     }
   }
 
-  // ---- staging: each wave issues kInstPerWave 1 KB direct-to-LDS loads per chunk
-  // buffer descriptor over this group's row tiles (base, stride 0, size, format word)
-  u32x4 rsrc;
+  // ---- this wave's records: every lane writes the source offset and x of
+  // its own rows that fall into one of them; lanes 0..3 mark padding rows
+  uint32_t* const src = s_src[wid];
+  uint32_t* const cx = s_cx[wid];
   {
-    const uint64_t base = (uint64_t)(uintptr_t)(a.planes + t0 * a.K + k0 * ct);
-    rsrc.x = __builtin_amdgcn_readfirstlane((uint32_t)base);
-    rsrc.y = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xFFFFu);
-    rsrc.z = __builtin_amdgcn_readfirstlane((uint32_t)((k1 - k0) * ct));
-    rsrc.w = kRsrcWord3;
-  }
-  uint8_t* const ring = reinterpret_cast<uint8_t*>(s_big);
-  uint8_t* const trash = ring + kRingBytes;
-  const int pps = pb / 16;                 // 16-byte pieces per slot (1..8)
-  // floor(n / pps) = (n * magic) >> 16 exactly for n < 8192, pps <= 8
-  const uint32_t pps_magic = (0x10000u + (uint32_t)pps - 1u) / (uint32_t)pps;
-  const int chunk_bytes = kChunkSlots * pb;
-  __syncthreads();   // s_qs, slot table, row tables visible
-
-  auto issue_chunk = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < kInstPerWave; ++i) {
-      const int j = kInstPerWave * wid + i;               // instruction slot within the chunk
-      const bool inst_ok = c < nchunks && j * 1024 < chunk_bytes;
-      const int piece = j * 64 + lane;                    // 16-byte piece within the chunk
-      const int sl = (int)(((uint32_t)piece * pps_magic) >> 16);   // slot within the chunk
-      const int s = c * kChunkSlots + sl;                           // plane slot
-      const bool ok = inst_ok && s < stot;
-      const uint32_t off = ok ? s_slot_off[s] + (uint32_t)((piece - sl * pps) * 16) : kOutOfRange;
-      uint8_t* dst = inst_ok ? ring + (c % kRingChunks) * chunk_bytes + j * 1024 : trash;
-      lds_load16(rsrc, dst, off);
+    int v = 1;
+    for (int j = 0; j < nrec; ++j) {
+      const int k = wid + kWaves * j;
+      while (k >= cbv[v + 1]) ++v;                 // width of couple k
+      const int nreal = cnt[v] - 4 * (k - cbv[v]); // rows present in this couple (>= 1)
+      if (lane >= nreal && lane < 4) {
+        src[4 * j + lane] = kOutOfRange;
+        reinterpret_cast<uint16_t*>(cx)[4 * j + lane] = 0;
+      }
     }
-  };
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t b = bq[e];
+    if (b > 0) {
+      int rank = 0, cb = 0;
+#pragma unroll
+      for (int v = 1; v <= 8; ++v) {
+        if (b == (uint32_t)v) {
+          rank = (e == 1 ? __popcll(msk[0][v]) : 0) +
+                 (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk[e][v] >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)msk[e][v], 0u));
+          cb = cbv[v];
+        }
+      }
+      const int k = cb + (rank >> 2);
+      if ((k & (kWaves - 1)) == wid) {
+        const int j = k / kWaves;
+        src[4 * j + (rank & 3)] = (uint32_t)rq[e] * (uint32_t)ct;
+        reinterpret_cast<uint16_t*>(cx)[4 * j + (rank & 3)] = xq[e];
+      }
+    }
+  }
 
-  const int lg = tid >> 5;
-  const int ll = tid & 31;
-  const bool lane_ok = ll < ct / 32;
+  // buffer descriptor over this group's row tiles of the tile block
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.planes + t0 * a.K + k0 * ct), (short)0, (int)((k1 - k0) * ct), kRsrcWord3);
+
   float acc[32];
 #pragma unroll
   for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
-  float h_acc = 0.0f, x_acc = 0.0f;   // this lane group's share of H and X
-
-  const bool full_tile = ct == kTile;
-  issue_chunk(0);
-  issue_chunk(1);
-  issue_chunk(2);
-  for (int c = 0; c < nchunks; ++c) {
-    // this wave's loads of chunk c are done once at most two later chunks'
-    // loads are outstanding; the barrier makes that true for every wave
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);
-    __syncthreads();
-    for (int q = s_qs[c] + lg; q < s_qs[c + 1]; q += kLaneGroups) {
-      const int e1 = 2 * q, e2 = 2 * q + 1;
-      const int b1 = s_b[e1];
-      const int b2 = e2 < m ? (int)s_b[e2] : 0;
-      const uint32_t x1h = s_xh[e1], x2h = e2 < m ? (uint32_t)s_xh[e2] : 0u;
-      const int sl1 = s_slot0[e1] % kRingSlots, sl2 = e2 < m ? (int)s_slot0[e2] % kRingSlots : 0;
-      const float x1 = half_bits_to_float((uint16_t)x1h), x2 = half_bits_to_float((uint16_t)x2h);
-      h_acc += phi_x(b1, x1) + phi_x(b2, x2);
-      x_acc += x1 + (b2 > 0 ? x2 : 0.0f);
-      const half2_t xv = __builtin_bit_cast(half2_t, x1h | (x2h << 16));
-      // Fast path: the whole wave has one width B for both rows, the tile is a
-      // full 1024 columns and neither row wraps around the ring end.
-      const int ub = __builtin_amdgcn_readfirstlane(b1);
-      const bool fast = __ballot(!(full_tile && b1 == ub && b2 == ub && sl1 + ub <= kRingSlots &&
-                                   sl2 + ub <= kRingSlots)) == 0;
-      if (fast) {
-        const uint8_t* r1 = ring + sl1 * 128 + 4 * ll;
-        const uint8_t* r2 = ring + sl2 * 128 + 4 * ll;
-        switch (ub) {
-          case 1: pair_fast<1>(r1, r2, xv, acc); break;
-          case 2: pair_fast<2>(r1, r2, xv, acc); break;
-          case 3: pair_fast<3>(r1, r2, xv, acc); break;
-          case 4: pair_fast<4>(r1, r2, xv, acc); break;
-          case 5: pair_fast<5>(r1, r2, xv, acc); break;
-          case 6: pair_fast<6>(r1, r2, xv, acc); break;
-          case 7: pair_fast<7>(r1, r2, xv, acc); break;
-          default: pair_fast<8>(r1, r2, xv, acc); break;
-        }
-      } else {
-        uint32_t w1[8], w2[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          w1[p] = (p < b1 && lane_ok) ? *reinterpret_cast<const uint32_t*>(ring + ((sl1 + p) % kRingSlots) * pb + 4 * ll) : 0u;
-          w2[p] = (p < b2 && lane_ok) ? *reinterpret_cast<const uint32_t*>(ring + ((sl2 + p) % kRingSlots) * pb + 4 * ll) : 0u;
-        }
-        uint32_t d1[8], d2[8];
-        rebuild_pair(b1, b2, w1, w2, d1, d2);
-        dot_pair(d1, d2, xv, acc);
-      }
-    }
-    __syncthreads();          // chunk c - 1 is no longer read: its ring place can be refilled
-    issue_chunk(c + 3);
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);   // trailing (empty) loads landed before the LDS is reused
-  __syncthreads();
-
-  // ---- reduce the 16 lane groups in LDS (row stride 33 keeps both the
-  // writes and the column-wise reads free of bank conflicts)
-  float* red = reinterpret_cast<float*>(s_big);
+  // the prologue's own loads (x, scale, zero) have landed long ago; from here
+  // on vmcnt counts only record loads
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   {
-    float* dst = red + (lg * 32 + ll) * kRedStride;
+    // width of record j: couples are in width order, so it only grows
+    int vj = 1;
+    auto width = [&](int j) {
+      const int k = wid + kWaves * j;
+      int v = vj;
+      while (k >= cbv[v + 1]) ++v;
+      return v;
+    };
+    RecordRegs ra, rb;
+    int ba = nrec > 0 ? width(0) : 0;
+    int bb = nrec > 1 ? width(1) : 0;
+    load_record(ra, rsrc, src, cx, 0, ba, pb);
+    load_record(rb, rsrc, src, cx, 1, bb, pb);
+    for (int j = 0; j < nrec; j += 2) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm16);   // record j landed; record j + 1 may be in flight
+      compute_record(ra, ba, acc);
+      vj = ba;
+      ba = j + 2 < nrec ? width(j + 2) : 0;
+      load_record(ra, rsrc, src, cx, j + 2, ba, pb);
+      if (j + 1 >= nrec) break;
+      __builtin_amdgcn_s_waitcnt(kWaitVm16);   // record j + 1 landed; record j + 2 may be in flight
+      compute_record(rb, bb, acc);
+      vj = bb;
+      bb = j + 3 < nrec ? width(j + 3) : 0;
+      load_record(rb, rsrc, src, cx, j + 3, bb, pb);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  // the two halves of a wave hold the same columns (different pairs)
+#pragma unroll
+  for (int c = 0; c < 32; ++c) acc[c] += __shfl_xor(acc[c], 32, 64);
+
+  // ---- reduce the 8 waves in LDS (row stride 33 keeps both the writes and
+  // the column-wise reads free of bank conflicts)
+  const int m = ncp;   // couples (0: no active row)
+  float* red = s_red;
+  if (lane < 32) {
+    float* dst = red + (wid * 32 + lane) * kRedStride;
 #pragma unroll
     for (int c = 0; c < 32; ++c) dst[c] = acc[c];
-    if (ll == 0) {
-      s_hx[lg][0] = h_acc;
-      s_hx[lg][1] = x_acc;
-    }
   }
   __syncthreads();
-  float H = 0.0f, X = 0.0f;
-#pragma unroll
-  for (int h = 0; h < kLaneGroups; ++h) {
-    H += s_hx[h][0];
-    X += s_hx[h][1];
-  }
+  const float H = s_hx[0];
+  const float X = s_hx[1];
   float val[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -471,7 +417,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
     if (m > 0 && col < ct && t0 + col < a.N) {
       float A = 0.0f;
 #pragma unroll
-      for (int h = 0; h < kLaneGroups; ++h) A += red[(h * 32 + (col >> 5)) * kRedStride + (col & 31)];
+      for (int h = 0; h < kWaves; ++h) A += red[(h * 32 + (col >> 5)) * kRedStride + (col & 31)];
       A *= 16777216.0f;   // codes entered as c * 2^-24
       val[u] = half_bits_to_float(sc[u]) * (A + H) + half_bits_to_float(zr[u]) * X;
     }
