@@ -17,8 +17,8 @@
 // Loads.  A lane loads its pair's plane words straight into registers with
 // 4-byte buffer loads: planes p < b come from the row tile, planes p >= b use
 // an out-of-range scalar offset, which returns 0 and moves no bytes, so only
-// the top b planes of a row are fetched.  Two records are in flight per
-// wave (double buffer); a wave waits only for its own loads and never for
+// the top b planes of a row are fetched.  Three records are in flight per
+// wave; a wave waits only for its own loads and never for
 // another wave until the final reduction.
 //
 // Compute.  The codes come back from the planes through a bit-transpose
@@ -53,7 +53,6 @@ constexpr int kScopeDevice = 16;                 // cache-policy bits: sc1 = dev
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14],
 // expcnt [6:4], lgkmcnt [11:8]; all-ones fields mean "do not wait".
 constexpr int kWaitVm0 = 0x0F70;                 // vmcnt(0) only
-constexpr int kWaitVm16 = 0x4F70;                // vmcnt(16) only: one record's loads may be outstanding
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -135,26 +134,24 @@ __device__ inline void dot_pair(const uint32_t (&d1)[8], const uint32_t (&d2)[8]
 // do not have are 0) and the pair's activations.
 struct RecordRegs {
   uint32_t w1[8], w2[8];
-  uint32_t xw;
 };
 
 // Issue the 16 loads of record j of this wave (width b; b = 0 for a record
 // the wave does not have) into r.  The record's row sources (byte offsets of
-// the row tiles within the group's block, out of range for padding rows) and
-// x pairs come from the wave's LDS tables.  Lane l of a pair loads plane word
+// the row tiles within the group's block, out of range for padding rows)
+// come from the wave's LDS table.  Lane l of a pair loads plane word
 // l of planes p < b of both rows (plane p at scalar offset p pb from the row
 // tile); planes p >= b get an out-of-range voffset, which returns 0 and moves
 // no bytes.  Only the voffset takes part in the range check, so it alone
 // carries the out-of-range value.  Every call issues exactly 16 loads, so the
 // wait counts of the pipeline are the same on every path.
 __device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, const uint32_t* src,
-                                   const uint32_t* cx, int j, int b, int pb) {
+                                   int j, int b, int pb) {
   const int h = (threadIdx.x >> 5) & 1;
   const int ll = threadIdx.x & 31;
   const int jj = j < kMaxRecords ? j : kMaxRecords - 1;   // table index (unused when b = 0)
   const uint32_t s1 = b > 0 ? src[4 * jj + 2 * h] : kOutOfRange;
   const uint32_t s2 = b > 0 ? src[4 * jj + 2 * h + 1] : kOutOfRange;
-  r.xw = b > 0 ? cx[2 * jj + h] : 0u;
   const uint32_t v1 = s1 == kOutOfRange ? kOutOfRange : s1 + 4u * (uint32_t)ll;
   const uint32_t v2 = s2 == kOutOfRange ? kOutOfRange : s2 + 4u * (uint32_t)ll;
 #pragma unroll
@@ -165,8 +162,9 @@ __device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, c
     r.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(p < b ? v2 : kOutOfRange), p * pb, 0);
 }
 
-// Rebuild and accumulate one record (width b, wave-uniform).
-__device__ inline void compute_record(const RecordRegs& r, int b, float (&acc)[32]) {
+// Rebuild and accumulate one record (width b, wave-uniform; xw: the pair's
+// two fp16 activations).
+__device__ inline void compute_record(const RecordRegs& r, int b, uint32_t xw, float (&acc)[32]) {
   uint32_t d1[8], d2[8];
   if (b <= 2) {
     planes_to_codes<2>(r.w1, d1);   // planes past b are 0 already
@@ -175,7 +173,16 @@ __device__ inline void compute_record(const RecordRegs& r, int b, float (&acc)[3
     planes_to_codes<8>(r.w1, d1);
     planes_to_codes<8>(r.w2, d2);
   }
-  dot_pair(d1, d2, __builtin_bit_cast(half2_t, r.xw), acc);
+  dot_pair(d1, d2, __builtin_bit_cast(half2_t, xw), acc);
+}
+
+// Bit width of couple k: the last width v whose first couple is <= k
+// (cbv is non-decreasing; empty widths share their successor's start).
+__device__ inline int couple_width(int k, const int (&cbv)[10]) {
+  int v = 1;
+#pragma unroll
+  for (int u = 2; u <= 8; ++u) v += k >= cbv[u] ? 1 : 0;
+  return v;
 }
 
 // Output modes.
@@ -321,11 +328,16 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
   uint32_t* const src = s_src[wid];
   uint32_t* const cx = s_cx[wid];
   {
-    int v = 1;
     for (int j = 0; j < nrec; ++j) {
       const int k = wid + kWaves * j;
-      while (k >= cbv[v + 1]) ++v;                 // width of couple k
-      const int nreal = cnt[v] - 4 * (k - cbv[v]); // rows present in this couple (>= 1)
+      const int v = couple_width(k, cbv);
+      int cv = 0, cbs = 0;
+#pragma unroll
+      for (int u = 1; u <= 8; ++u) {
+        cv = u == v ? cnt[u] : cv;
+        cbs = u == v ? cbv[u] : cbs;
+      }
+      const int nreal = cv - 4 * (k - cbs);        // rows present in this couple (>= 1)
       if (lane >= nreal && lane < 4) {
         src[4 * j + lane] = kOutOfRange;
         reinterpret_cast<uint16_t*>(cx)[4 * j + lane] = 0;
@@ -366,31 +378,27 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
   // on vmcnt counts only record loads
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   {
-    // width of record j: couples are in width order, so it only grows
-    int vj = 1;
-    auto width = [&](int j) {
-      const int k = wid + kWaves * j;
-      int v = vj;
-      while (k >= cbv[v + 1]) ++v;
-      return v;
-    };
-    RecordRegs ra, rb;
-    int ba = nrec > 0 ? width(0) : 0;
-    int bb = nrec > 1 ? width(1) : 0;
-    load_record(ra, rsrc, src, cx, 0, ba, pb);
-    load_record(rb, rsrc, src, cx, 1, bb, pb);
-    for (int j = 0; j < nrec; j += 2) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm16);   // record j landed; record j + 1 may be in flight
-      compute_record(ra, ba, acc);
-      vj = ba;
-      ba = j + 2 < nrec ? width(j + 2) : 0;
-      load_record(ra, rsrc, src, cx, j + 2, ba, pb);
-      if (j + 1 >= nrec) break;
-      __builtin_amdgcn_s_waitcnt(kWaitVm16);   // record j + 1 landed; record j + 2 may be in flight
-      compute_record(rb, bb, acc);
-      vj = bb;
-      bb = j + 3 < nrec ? width(j + 3) : 0;
-      load_record(rb, rsrc, src, cx, j + 3, bb, pb);
+    // Three records in flight.  The record sequence is unrolled (a wave has
+    // at most kMaxRecords) so that the load order is static: record j + 3 is
+    // issued into the registers of record j right after j is consumed, and
+    // the compiler's wait counts let j + 1 and j + 2 stay outstanding.
+    // Records past nrec load nothing (width 0) and are not computed.
+    const int h = (tid >> 5) & 1;
+    auto width = [&](int j) { return j < nrec ? couple_width(wid + kWaves * j, cbv) : 0; };
+    RecordRegs rr[3];
+    int bw[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      bw[j] = width(j);
+      load_record(rr[j], rsrc, src, j, bw[j], pb);
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxRecords; ++j) {
+      if (j < nrec) compute_record(rr[j % 3], bw[j % 3], cx[2 * j + h], acc);
+      if (j + 3 < kMaxRecords) {
+        bw[j % 3] = width(j + 3);
+        load_record(rr[j % 3], rsrc, src, j + 3, bw[j % 3], pb);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
