@@ -2,11 +2,19 @@
 
 One step = one decode-stage VMM of one linear layer at batch 1: precision
 assignment from |x| and calibrated thresholds, active-row selection, bit-plane
-streaming, reconstruction, dequantisation, fp32 accumulation and the split-K
-reduction (the fused ``grinqh_decode_vmm`` launch).  Inputs are resident in
-HBM before timing starts; every step reads a different copy of the layer
-(planes, scales, zeros, x) so that the working set (>= 512 MB) cannot sit in
-the 256 MB Infinity Cache.
+streaming, reconstruction, dequantisation and fp32 accumulation, in one
+launch.  The default entry point is ``grinqh_decode_vmm_accumulate`` used the
+way a decode loop uses it: each step adds x W into an output buffer that the
+previous step zeroed, and zeroes the other one for the next step (ping-pong),
+so every step produces a complete y = x W.  ``--mode decode`` times
+``grinqh_decode_vmm`` (deterministic split-K reduction) instead; the default
+run reports both.
+
+Inputs are resident in HBM before timing starts; every step reads a different
+copy of the layer (planes, scales, zeros, x) so that the working set (>= 512
+MB) cannot sit in the 256 MB Infinity Cache.  Steps are captured once in a HIP
+graph and replayed; the time per step comes from HIP events recorded on the
+stream the kernels run on, around one replay.
 
 Prints one JSON line.  ``value`` is the achieved bandwidth over algorithmic
 bytes (sum_i b_i N_pad / 8 plane bytes + 4 N bytes of fp16 scale and zero per
@@ -15,29 +23,43 @@ active group + 2 K bytes of x) per step, in GB/s.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 ROT_BYTES = 512 << 20
 
+# name: (K, N, config, matrix, P key, level set)
 WORKLOADS = {
-    # name: (K, N, config, matrix, P key, levels)
     "llama3-8b-gate-4096x14336-avg3": (4096, 14336, 2, 4, 3, "5"),
     "llama3-8b-gate-4096x14336-avg2": (4096, 14336, 2, 4, 2, "5"),
     "llama3-8b-gate-4096x14336-avg4": (4096, 14336, 2, 4, 4, "5"),
+    "llama3-8b-gate-4096x14336-avg8": (4096, 14336, 2, 4, 8, "5"),
+    "llama3-8b-down-14336x4096-avg3": (14336, 4096, 2, 6, 3, "5"),
     "attn-proj-4096x4096-avg2": (4096, 4096, 1, 0, 2, "5"),
     "attn-proj-4096x4096-avg3": (4096, 4096, 1, 0, 3, "5"),
     "attn-proj-4096x4096-avg4": (4096, 4096, 1, 0, 4, "5"),
     "attn-proj-4096x4096-avg8": (4096, 4096, 1, 0, 8, "5"),
 }
+for _b in ("0.5", "1", "2", "3", "4", "6", "8"):
+    WORKLOADS[f"llama3-70b-gate-8192x28672-avg{_b}"] = (8192, 28672, 4, 0, float(_b), "4")
+    WORKLOADS[f"llama3-70b-down-28672x8192-avg{_b}"] = (28672, 8192, 4, 1, float(_b), "4")
 DEFAULT = "llama3-8b-gate-4096x14336-avg3"
-SWEEP = ["attn-proj-4096x4096-avg2", "attn-proj-4096x4096-avg3", "attn-proj-4096x4096-avg4",
-         "attn-proj-4096x4096-avg8", "llama3-8b-gate-4096x14336-avg2", "llama3-8b-gate-4096x14336-avg4"]
+SWEEP = ([f"attn-proj-4096x4096-avg{b}" for b in (2, 3, 4, 8)]
+         + [f"llama3-8b-gate-4096x14336-avg{b}" for b in (2, 3, 4, 8)]
+         + [f"llama3-70b-gate-8192x28672-avg{b}" for b in ("0.5", "1", "2", "3", "4", "6", "8")])
+ENTRY = {"accumulate": "grinqh_decode_vmm_accumulate", "decode": "grinqh_decode_vmm"}
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "vmm_traffic_*.md")
+KERNEL_SOURCES = ("decode_stage_gemv_amd/csrc/vmm.hip", "decode_stage_gemv_amd/csrc/bitplane.hpp",
+                  "decode_stage_gemv_amd/csrc/common.hpp")
 
 
 def log(msg):
@@ -46,62 +68,97 @@ def log(msg):
 
 def _P(key, levels):
     import synthetic
-    return (synthetic.P_LEVELS_5 if levels == "5" else synthetic.P_LEVELS_4)[key], \
-        (synthetic.LEVELS_5 if levels == "5" else synthetic.LEVELS_4)
+    table = synthetic.P_LEVELS_5 if levels == "5" else synthetic.P_LEVELS_4
+    lv = synthetic.LEVELS_5 if levels == "5" else synthetic.LEVELS_4
+    return table[key], lv
 
 
-class Prepared:
-    """A layer resident on the GPU in R rotated copies, thresholds calibrated on the GPU."""
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
-    def __init__(self, name, mode="decode"):
+
+def measured_traffic(workload, mode):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
+
+    The summary states the kernel-source hash it was taken with; a summary of
+    older kernel sources does not count."""
+    want = kernel_source_hash()
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        text = open(path).read()
+        m_w = re.search(r"^workload:\s*(\S+)", text, re.M)
+        m_m = re.search(r"^entry point:\s*(\S+)", text, re.M)
+        m_h = re.search(r"^kernel sources sha256:\s*([0-9a-f]{64})", text, re.M)
+        m_t = re.search(r"^traffic bytes per launch:\s*([0-9.]+)", text, re.M)
+        if not (m_w and m_m and m_h and m_t):
+            continue
+        if m_w.group(1) == workload and m_m.group(1) == ENTRY[mode] and m_h.group(1) == want:
+            return float(m_t.group(1))
+    return None
+
+
+class Layer:
+    """One synthetic layer packed on the GPU, in R rotated copies."""
+
+    def __init__(self, K, N, cfg, mat, copies_bytes=ROT_BYTES):
         import torch
         import synthetic
         import decode_stage_gemv_amd as grq
-        K, N, cfg, mat, pkey, lv = WORKLOADS[name]
-        self.name, self.K, self.N = name, K, N
-        self.P, self.levels = _P(pkey, lv)
         t0 = time.time()
+        self.K, self.N, self.cfg, self.mat = K, N, cfg, mat
         lay = synthetic.make_layer(K, N, config=cfg, matrix=mat, n_test=1)
         dev = torch.device("cuda:0")
         planes = grq.pack(torch.from_numpy(lay.codes).to(dev))
         scales = torch.from_numpy(lay.scales).to(dev)
         zeros = torch.from_numpy(lay.zeros).to(dev)
-        calib = torch.from_numpy(lay.calib).to(dev)
-        th_dev = grq.calibrate(calib, self.P)
-        self.thresholds = [float(v) for v in th_dev.cpu().numpy()]
+        self.calib = torch.from_numpy(lay.calib).to(dev)
         per_copy = planes.numel() + 2 * scales.numel() * 2 + 2 * K
-        self.R = max(1, -(-ROT_BYTES // per_copy))
-        xs = synthetic.make_activations(K, self.R, config=cfg, matrix=mat)
-        self.copies = []
-        for r in range(self.R):
-            self.copies.append((planes.clone(), scales.clone(), zeros.clone(),
-                                torch.from_numpy(xs[r]).to(dev)))
-        del planes
+        self.R = max(1, -(-copies_bytes // per_copy))
+        self.xs_host = synthetic.make_activations(K, self.R, config=cfg, matrix=mat)
+        self.copies = [(planes if r == 0 else planes.clone(), scales.clone(), zeros.clone(),
+                        torch.from_numpy(self.xs_host[r]).to(dev)) for r in range(self.R)]
+        self.host = lay
+        self.np_cols = int(grq.lib().grinqh_planes_bytes(1, N))
+        torch.cuda.synchronize()
+        log(f"layer {K}x{N}: R={self.R} copies, setup {time.time() - t0:.1f}s")
+
+
+class Prepared:
+    """A workload: a layer, thresholds calibrated on the GPU for its level mix."""
+
+    def __init__(self, name, mode="accumulate", layer=None):
+        import torch
+        import decode_stage_gemv_amd as grq
+        K, N, cfg, mat, pkey, lv = WORKLOADS[name]
+        self.name, self.K, self.N, self.mode = name, K, N, mode
+        self.P, self.levels = _P(pkey, lv)
+        self.layer = layer if layer is not None else Layer(K, N, cfg, mat)
+        self.R = self.layer.R
+        self.thresholds = [float(v) for v in grq.calibrate(self.layer.calib, self.P).cpu().numpy()]
+        dev = torch.device("cuda:0")
         self.ws = grq.make_workspace(K, N)
         self.y = torch.empty(N, dtype=torch.float32, device=dev)
-        self.mode = mode
         self.ybufs = [torch.zeros(N, dtype=torch.float32, device=dev) for _ in range(2)]
         # algorithmic bytes of each copy's step, from the GPU's own assignment
-        self.bytes = []
-        self.avg_bits = []
-        Np = (N + 31) // 32 * 32
+        self.bytes, self.avg_bits = [], []
         G = (K + 127) // 128
-        for (_, _, _, x) in self.copies:
+        for (_, _, _, x) in self.layer.copies:
             bits, _, _ = grq.assign_bits(x, self.thresholds, self.levels)
             b = bits.to(torch.int64)
             pad = torch.zeros(G * 128 - K, dtype=torch.int64, device=dev)
             active_groups = int((torch.cat([b, pad]).view(G, 128).amax(dim=1) > 0).sum().item())
-            self.bytes.append(int(b.sum().item()) * Np // 8 + 4 * N * active_groups + 2 * K)
+            self.bytes.append(int(b.sum().item()) * self.layer.np_cols // 8 + 4 * N * active_groups + 2 * K)
             self.avg_bits.append(float(b.sum().item()) / K)
-        self.host_x = xs
-        self.host_layer = lay
         torch.cuda.synchronize()
-        log(f"prepared {name}: R={self.R} copies, avg bits {np.mean(self.avg_bits):.3f}, "
-            f"{np.mean(self.bytes) / 1e6:.2f} MB/step, setup {time.time() - t0:.1f}s")
+        log(f"prepared {name} ({ENTRY[mode]}): avg bits {np.mean(self.avg_bits):.3f}, "
+            f"{np.mean(self.bytes) / 1e6:.2f} MB/step")
 
     def step(self, k):
         import decode_stage_gemv_amd as grq
-        planes, scales, zeros, x = self.copies[k % self.R]
+        planes, scales, zeros, x = self.layer.copies[k % self.R]
         if self.mode == "accumulate":
             # decode-loop ping-pong: add into one buffer, clear the other for the next step
             grq.decode_vmm_accumulate(planes, scales, zeros, x, self.K, self.N, self.thresholds,
@@ -174,13 +231,14 @@ def copy_probe(nbytes=512 << 20, reps=20):
 
 
 def cpu_baseline(prep, budget_s=15.0):
-    """The oracle's decode step (assign, select, fp64 VMM) on the host cores."""
+    """The oracle's decode step (assign, select, fp64 VMM) on the host cores,
+    over whole steps of the same workload until about budget_s of host time."""
     import oracle
-    lay = prep.host_layer
+    lay = prep.layer.host
     th = np.asarray(prep.thresholds, np.float32)
     n, t_total, bytes_total = 0, 0.0, 0.0
     while t_total < budget_s and n < 50:
-        x = prep.host_x[n % prep.R]
+        x = prep.layer.xs_host[n % prep.R]
         t0 = time.perf_counter()
         oracle.decode_step(lay.codes, lay.scales, lay.zeros, x, th, prep.levels)
         t_total += time.perf_counter() - t0
@@ -189,8 +247,19 @@ def cpu_baseline(prep, budget_s=15.0):
     cores = len(os.sched_getaffinity(0))
     return {"value": bytes_total / t_total / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "us_per_vmm": t_total / n * 1e6,
-            "sample": f"{n} full decode steps of {prep.name} (assign + select + fp64 VMM), "
-                      f"{t_total:.1f}s of host time"}
+            "sample": f"{n} whole decode steps of {prep.name} (assign + select + fp64 VMM, "
+                      f"numpy), {t_total:.1f}s of host time"}
+
+
+def linear_fit(points):
+    """Least squares us = a + bytes / BW over (bytes, us) points."""
+    b = np.array([p[0] for p in points], np.float64)
+    t = np.array([p[1] for p in points], np.float64)
+    A = np.stack([np.ones_like(b), b], axis=1)
+    (a, slope), *_ = np.linalg.lstsq(A, t, rcond=None)
+    pred = a + slope * b
+    r2 = 1.0 - float(np.sum((t - pred) ** 2)) / max(float(np.sum((t - t.mean()) ** 2)), 1e-30)
+    return {"intercept_us": float(a), "bw_eff_GB_s": float(1e-3 / slope) if slope > 0 else None, "r2": r2}
 
 
 def main():
@@ -199,18 +268,20 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--sweep", action="store_true", help="also time the bit-width sweep")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the bit-width sweep (4096^2, 4096x14336, 70B gate at 0.5..8 bits)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
-    ap.add_argument("--mode", choices=["decode", "accumulate"], default="decode",
-                    help="decode: grinqh_decode_vmm (deterministic split-K); "
-                         "accumulate: grinqh_decode_vmm_accumulate (fp32 atomics, ping-pong outputs)")
+    ap.add_argument("--mode", choices=sorted(ENTRY), default="accumulate",
+                    help="accumulate: grinqh_decode_vmm_accumulate (ping-pong outputs); "
+                         "decode: grinqh_decode_vmm (deterministic split-K)")
+    ap.add_argument("--only", action="store_true", help="time only the chosen entry point")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 512 MiB device copy (reference for bandwidth and counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the decode VMM path here is single-GPU "
-              "(multi-GPU sharding is a design note only); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: this decode VMM path runs on a single GPU "
+              "(sharding across GPUs is a design note only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -225,21 +296,45 @@ def main():
     if args.no_graph:
         log("host-launched steps (no graph): includes Python and ctypes launch overhead")
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"{args.workload}: {ms * 1e3:.2f} us/VMM, {gbs:.1f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+    log(f"{args.workload} {ENTRY[args.mode]}: {ms * 1e3:.2f} us/VMM, {gbs:.1f} GB/s "
+        f"({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+
+    others = {}
+    if not args.only:
+        for mode in sorted(ENTRY):
+            if mode == args.mode:
+                continue
+            p = Prepared(args.workload, mode, layer=prep.layer)
+            m, b = p.run(args.steps, args.warmup, graph=not args.no_graph)
+            others[ENTRY[mode]] = {"us_per_vmm": m * 1e3, "GB_s": b / (m * 1e-3) / 1e9}
+            log(f"{args.workload} {ENTRY[mode]}: {m * 1e3:.2f} us/VMM, {others[ENTRY[mode]]['GB_s']:.1f} GB/s")
+            del p
 
     sweep = {}
     if args.sweep:
+        layers = {}
         for name in SWEEP:
-            p = Prepared(name, args.mode)
-            m, b = p.run(args.steps, args.warmup)
+            K, N, cfg, mat, _, _ = WORKLOADS[name]
+            key = (K, N, cfg, mat)
+            if key not in layers:
+                layers.clear()
+                torch.cuda.empty_cache()
+                layers[key] = Layer(K, N, cfg, mat)
+            p = Prepared(name, args.mode, layer=layers[key])
+            m, b = p.run(min(args.steps, 100), args.warmup)
             sweep[name] = {"us_per_vmm": m * 1e3, "GB_s": b / (m * 1e-3) / 1e9,
                            "frac_of_peak": b / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
                            "avg_bits": float(np.mean(p.avg_bits)), "bytes": b}
-            log(f"{name}: {m * 1e3:.2f} us/VMM, {sweep[name]['GB_s']:.1f} GB/s")
+            log(f"{name}: {m * 1e3:.2f} us/VMM, {sweep[name]['GB_s']:.1f} GB/s, avg bits {sweep[name]['avg_bits']:.2f}")
             del p
-            torch.cuda.empty_cache()
+        layers.clear()
+        fit_pts = [(v["bytes"], v["us_per_vmm"]) for k, v in sweep.items() if k.startswith("llama3-70b-gate")]
+        if len(fit_pts) >= 3:
+            sweep["linear_fit_70b_gate"] = linear_fit(fit_pts)
+            log(f"70B gate linear fit: {sweep['linear_fit_70b_gate']}")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(prep)
+    traffic = measured_traffic(args.workload, args.mode)
     out = {
         "metric": "µs per VMM and achieved HBM GB/s (% of peak) at avg 2/3/4/8 bits, batch 1",
         "value": gbs,
@@ -252,15 +347,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8 planes, fp16 x/scale/zero, fp32 accumulate",
-        "data": "synthetic (seeded N(0,0.02) weights, RTN 8-bit, log-normal x with 1% outlier channels)",
-        "config": {"workload": args.workload, "entry_point": "grinqh_decode_vmm" if args.mode == "decode" else "grinqh_decode_vmm_accumulate", "K": prep.K, "N": prep.N,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,0.02) weights, RTN 8-bit codes, log-normal |x| with 1% outlier channels)",
+        "config": {"workload": args.workload, "entry_point": ENTRY[args.mode], "K": prep.K, "N": prep.N,
                    "avg_bits": float(np.mean(prep.avg_bits)), "bytes_per_step": step_bytes,
-                   "rotated_copies": prep.R, "thresholds": prep.thresholds, "levels": list(prep.levels)},
+                   "rotated_copies": prep.R, "graph_replay": not args.no_graph,
+                   "arithmetic": "fp16 x times 8-bit codes (as fp16 subnormals) into fp32 accumulators, fp32 dequant",
+                   "thresholds": prep.thresholds, "levels": list(prep.levels)},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": cpu,
     }
+    if others:
+        out["other_entry_points"] = others
     if sweep:
         out["sweep"] = sweep
     print(json.dumps(out), flush=True)

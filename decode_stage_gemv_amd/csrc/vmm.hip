@@ -166,9 +166,13 @@ __device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, c
 // two fp16 activations).
 __device__ inline void compute_record(const RecordRegs& r, int b, uint32_t xw, float (&acc)[32]) {
   uint32_t d1[8], d2[8];
+  // planes past b are 0 already; the networks for 2 and 3 planes skip them
   if (b <= 2) {
-    planes_to_codes<2>(r.w1, d1);   // planes past b are 0 already
+    planes_to_codes<2>(r.w1, d1);
     planes_to_codes<2>(r.w2, d2);
+  } else if (b == 3) {
+    planes_to_codes<3>(r.w1, d1);
+    planes_to_codes<3>(r.w2, d2);
   } else {
     planes_to_codes<8>(r.w1, d1);
     planes_to_codes<8>(r.w2, d2);
