@@ -30,14 +30,21 @@ int main() {
       grinqh::planes_to_codes_rt(b, wb, d);
       uint32_t d8[8];
       grinqh::planes_to_codes<8>(wb, d8);                      // the generic network agrees
+      // the VMM's choice: the 2-plane network for b <= 2, the 3-plane one for
+      // b = 3 and the full one above, always with the missing planes zero
+      uint32_t dv[8];
+      if (b <= 2) grinqh::planes_to_codes<2>(wb, dv);
+      else if (b == 3) grinqh::planes_to_codes<3>(wb, dv);
+      else grinqh::planes_to_codes<8>(wb, dv);
       const unsigned mask = b == 0 ? 0u : (0xFFu << (8 - b)) & 0xFFu;
       for (int c = 0; c < 32; ++c) {
         const int m = c / 4, j = c % 4;
         const unsigned got = (d[m] >> (8 * j)) & 0xFFu;
         const unsigned got8 = (d8[m] >> (8 * j)) & 0xFFu;
+        const unsigned gotv = (dv[m] >> (8 * j)) & 0xFFu;
         const unsigned want = code[c] & mask;
-        if (got != want || got8 != want) {
-          printf("FAIL trial %d b %d col %d: got %02x/%02x want %02x\n", trial, b, c, got, got8, want);
+        if (got != want || got8 != want || gotv != want) {
+          printf("FAIL trial %d b %d col %d: got %02x/%02x/%02x want %02x\n", trial, b, c, got, got8, gotv, want);
           return 1;
         }
         ++checked;

@@ -202,22 +202,47 @@ def test_bytes_read_accounting():
 
 # ------------------------------------------------ the pins catch planted mistakes
 
-def test_planted_mistakes_are_caught(monkeypatch):
-    """Plant plausible mistakes in the oracle and check a pin fails for each."""
+def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
+    """Plant plausible mistakes in the oracle and check a pin fails for each:
+    a dropped or sign-flipped midpoint, an off-by-one width, a dropped zero
+    term, a transposed weight operand and a wrong group size."""
     codes, scales, zeros, x = _rand_case(8, 8, 77)
     bits = np.array([1, 2, 3, 4, 5, 6, 7, 8], np.uint8)
     good = grinqh_oracle.reconstruct_level
+    good_rows = grinqh_oracle._dequant_rows
 
     def no_phi(q, b):
         step = float(2 ** (8 - b))
         return np.floor(np.asarray(q, np.float64) / step) * step
 
+    def minus_phi(q, b):
+        return 2 * no_phi(q, b) - good(q, b) if 0 < b < 8 else good(q, b)
+
     def off_by_one_shift(q, b):
         return good(q, min(b + 1, 8))
 
-    for bad in (no_phi, off_by_one_shift):
+    for bad in (no_phi, minus_phi, off_by_one_shift):
         monkeypatch.setattr(grinqh_oracle, "reconstruct_level", bad)
         with pytest.raises(AssertionError):
             _check_exact(codes, scales, zeros, x, bits)
     monkeypatch.setattr(grinqh_oracle, "reconstruct_level", good)
+
+    def no_zero_term(codes_, scales_, zeros_, rows, bits_):
+        return good_rows(codes_, scales_, np.zeros_like(zeros_), rows, bits_)
+
+    def transposed(codes_, scales_, zeros_, rows, bits_):
+        return good_rows(np.ascontiguousarray(codes_.T), scales_, zeros_, rows, bits_)
+
+    for bad in (no_zero_term, transposed):
+        monkeypatch.setattr(grinqh_oracle, "_dequant_rows", bad)
+        with pytest.raises(AssertionError):
+            _check_exact(codes, scales, zeros, x, bits)
+    monkeypatch.setattr(grinqh_oracle, "_dequant_rows", good_rows)
     _check_exact(codes, scales, zeros, x, bits)
+
+    # a wrong group size is caught by the hand-worked two-group golden case
+    monkeypatch.setattr(grinqh_oracle, "GROUP", 256)
+    with pytest.raises(AssertionError):
+        test_vmm_golden_two_groups(golden_dir)
+    monkeypatch.setattr(grinqh_oracle, "GROUP", 128)
+    test_vmm_golden_two_groups(golden_dir)
