@@ -139,12 +139,13 @@ struct RecordRegs {
 // Issue the 16 loads of record j of this wave (width b; b = 0 for a record
 // the wave does not have) into r.  The record's row sources (byte offsets of
 // the row tiles within the group's block, out of range for padding rows)
-// come from the wave's LDS table.  Lane l of a pair loads plane word
-// l of planes p < b of both rows (plane p at scalar offset p pb from the row
-// tile); planes p >= b get an out-of-range voffset, which returns 0 and moves
-// no bytes.  Only the voffset takes part in the range check, so it alone
-// carries the out-of-range value.  Every call issues exactly 16 loads, so the
-// wait counts of the pipeline are the same on every path.
+// come from the wave's LDS table.  Lane l of a pair loads plane word l of
+// planes p < b of both rows (plane p at scalar offset p pb from the row
+// tile).  Every call issues exactly 16 loads so that the wait counts of the
+// pipeline are the same on every path: the loads of planes p >= b repeat
+// plane 0 (a cache hit; compute_record ignores them), and a padding row or a
+// record the wave does not have uses an out-of-range voffset, which returns
+// 0 and moves no bytes (only the voffset takes part in the range check).
 __device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, const uint32_t* src,
                                    int j, int b, int pb) {
   const int h = (threadIdx.x >> 5) & 1;
@@ -156,26 +157,31 @@ __device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, c
   const uint32_t v2 = s2 == kOutOfRange ? kOutOfRange : s2 + 4u * (uint32_t)ll;
 #pragma unroll
   for (int p = 0; p < 8; ++p)
-    r.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(p < b ? v1 : kOutOfRange), p * pb, 0);
+    r.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)v1, p < b ? p * pb : 0, 0);
 #pragma unroll
   for (int p = 0; p < 8; ++p)
-    r.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)(p < b ? v2 : kOutOfRange), p * pb, 0);
+    r.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)v2, p < b ? p * pb : 0, 0);
 }
 
-// Rebuild and accumulate one record (width b, wave-uniform; xw: the pair's
-// two fp16 activations).
+// Rebuild and accumulate one record (width b >= 1, wave-uniform): the
+// network for exactly b planes, so planes at or past b are never read.
+template <int B>
+__device__ inline void rebuild_pair(const RecordRegs& r, uint32_t (&d1)[8], uint32_t (&d2)[8]) {
+  planes_to_codes<B>(r.w1, d1);
+  planes_to_codes<B>(r.w2, d2);
+}
+
 __device__ inline void compute_record(const RecordRegs& r, int b, uint32_t xw, float (&acc)[32]) {
   uint32_t d1[8], d2[8];
-  // planes past b are 0 already; the networks for 2 and 3 planes skip them
-  if (b <= 2) {
-    planes_to_codes<2>(r.w1, d1);
-    planes_to_codes<2>(r.w2, d2);
-  } else if (b == 3) {
-    planes_to_codes<3>(r.w1, d1);
-    planes_to_codes<3>(r.w2, d2);
-  } else {
-    planes_to_codes<8>(r.w1, d1);
-    planes_to_codes<8>(r.w2, d2);
+  switch (b) {
+    case 1: rebuild_pair<1>(r, d1, d2); break;
+    case 2: rebuild_pair<2>(r, d1, d2); break;
+    case 3: rebuild_pair<3>(r, d1, d2); break;
+    case 4: rebuild_pair<4>(r, d1, d2); break;
+    case 5: rebuild_pair<5>(r, d1, d2); break;
+    case 6: rebuild_pair<6>(r, d1, d2); break;
+    case 7: rebuild_pair<7>(r, d1, d2); break;
+    default: rebuild_pair<8>(r, d1, d2); break;
   }
   dot_pair(d1, d2, __builtin_bit_cast(half2_t, xw), acc);
 }
