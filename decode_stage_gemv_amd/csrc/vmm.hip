@@ -186,15 +186,6 @@ __device__ inline void compute_record(const RecordRegs& r, int b, uint32_t xw, f
   dot_pair(d1, d2, __builtin_bit_cast(half2_t, xw), acc);
 }
 
-// Bit width of couple k: the last width v whose first couple is <= k
-// (cbv is non-decreasing; empty widths share their successor's start).
-__device__ inline int couple_width(int k, const int (&cbv)[10]) {
-  int v = 1;
-#pragma unroll
-  for (int u = 2; u <= 8; ++u) v += k >= cbv[u] ? 1 : 0;
-  return v;
-}
-
 // Output modes.
 enum : int {
   kOutSplitK = 0,     // partial rows + last-arriving workgroup adds them in split order
@@ -337,10 +328,16 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
   // its own rows that fall into one of them; lanes 0..3 mark padding rows
   uint32_t* const src = s_src[wid];
   uint32_t* const cx = s_cx[wid];
+  // lane j < kMaxRecords describes record j (couple wid + 8 j): its width
+  // (0 if the wave has no such record) and, for a width's last couple, the
+  // padding places, all in vector registers at once
+  int rec_w = 0;
   {
-    for (int j = 0; j < nrec; ++j) {
-      const int k = wid + kWaves * j;
-      const int v = couple_width(k, cbv);
+    const int k = wid + kWaves * lane;
+    if (lane < kMaxRecords && k < ncp) {
+      int v = 1;
+#pragma unroll
+      for (int u = 2; u <= 8; ++u) v += k >= cbv[u] ? 1 : 0;
       int cv = 0, cbs = 0;
 #pragma unroll
       for (int u = 1; u <= 8; ++u) {
@@ -348,10 +345,11 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
         cbs = u == v ? cbv[u] : cbs;
       }
       const int nreal = cv - 4 * (k - cbs);        // rows present in this couple (>= 1)
-      if (lane >= nreal && lane < 4) {
-        src[4 * j + lane] = kOutOfRange;
-        reinterpret_cast<uint16_t*>(cx)[4 * j + lane] = 0;
+      for (int t = nreal; t < 4; ++t) {
+        src[4 * lane + t] = kOutOfRange;
+        reinterpret_cast<uint16_t*>(cx)[4 * lane + t] = 0;
       }
+      rec_w = v;
     }
   }
 #pragma unroll
@@ -394,7 +392,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
     // the compiler's wait counts let j + 1 and j + 2 stay outstanding.
     // Records past nrec load nothing (width 0) and are not computed.
     const int h = (tid >> 5) & 1;
-    auto width = [&](int j) { return j < nrec ? couple_width(wid + kWaves * j, cbv) : 0; };
+    auto width = [&](int j) { return j < kMaxRecords ? __builtin_amdgcn_readlane(rec_w, j) : 0; };
     RecordRegs rr[3];
     int bw[3];
 #pragma unroll
