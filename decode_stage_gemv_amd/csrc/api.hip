@@ -42,6 +42,13 @@ static int check_assign_params(const float* thresholds, const uint8_t* levels, i
     if (levels[t] > GRINQH_MAX_BITS) return fail(GRINQH_EINVAL, "level %d is %u (must be 0..8)", t, (unsigned)levels[t]);
     ap->lv[t] = levels[t];
   }
+  // Unused slots: thresholds +inf and levels[n] repeated, so the kernels
+  // compare against all kMaxThresholds slots without looking at n (a finite
+  // |x| never reaches +inf; +inf reaches every slot and still gets levels[n]).
+  for (int t = n; t < kMaxThresholds; ++t) {
+    ap->th[t] = INFINITY;
+    ap->lv[t + 1] = levels[n];
+  }
   return GRINQH_OK;
 }
 

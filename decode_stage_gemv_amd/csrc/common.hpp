@@ -15,8 +15,8 @@ constexpr int kMaxThresholds = GRINQH_MAX_THRESHOLDS;
 
 // Thresholds and levels travel as a kernel argument (a few SGPR loads).
 struct AssignParams {
-  float th[kMaxThresholds];
-  uint32_t lv[kMaxThresholds + 1];   // 32-bit so the kernel reads them with scalar loads
+  float th[kMaxThresholds];          // slots past n: +inf
+  uint32_t lv[kMaxThresholds + 1];   // slots past n: levels[n]; 32-bit for scalar loads
   int n;
 };
 
@@ -28,50 +28,35 @@ __device__ inline float half_bits_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-// Level index for one activation: number of thresholds |x| reaches (fp32).
-__device__ inline int level_of(uint16_t xh, const AssignParams& ap) {
-  const float ax = __builtin_fabsf(half_bits_to_float(xh));
-  int k = 0;
-#pragma unroll
-  for (int t = 0; t < kMaxThresholds; ++t) k += (t < ap.n && ax >= ap.th[t]) ? 1 : 0;
-  return k;
-}
-
-// b_i = levels[k] with compile-time indices only (thresholds are non-decreasing,
-// so k thresholds reached means the first k).
-__device__ inline uint32_t level_bits(int k, const AssignParams& ap) {
-  uint32_t b = ap.lv[0];
-#pragma unroll
-  for (int t = 1; t <= kMaxThresholds; ++t) b = (k >= t) ? (uint32_t)ap.lv[t] : b;
-  return b;
-}
-
-// Thresholds and levels held in wave-uniform registers (read once per kernel).
+// Thresholds and level steps held in wave-uniform registers (read once per
+// kernel): step[t] = levels[t + 1] - levels[t].
 struct AssignRegs {
   float th[kMaxThresholds];
-  uint32_t lv[kMaxThresholds + 1];
-  int n;
+  int step[kMaxThresholds];
+  int lv0;
 };
 
 __device__ inline AssignRegs load_assign_regs(const AssignParams& ap) {
   AssignRegs r;
 #pragma unroll
-  for (int t = 0; t < kMaxThresholds; ++t)
+  for (int t = 0; t < kMaxThresholds; ++t) {
     r.th[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, ap.th[t])));
-#pragma unroll
-  for (int t = 0; t <= kMaxThresholds; ++t) r.lv[t] = __builtin_amdgcn_readfirstlane(ap.lv[t]);
-  r.n = __builtin_amdgcn_readfirstlane(ap.n);
+    r.step[t] = __builtin_amdgcn_readfirstlane((int)ap.lv[t + 1] - (int)ap.lv[t]);
+  }
+  r.lv0 = __builtin_amdgcn_readfirstlane((int)ap.lv[0]);
   return r;
 }
 
-// b = levels[#thresholds reached]; with non-decreasing thresholds the reached
-// ones are a prefix, so the last one reached names the level.
+// b = levels[#thresholds reached].  With non-decreasing thresholds the
+// reached ones are a prefix, so b = levels[0] plus the steps of the reached
+// thresholds (a sum, so no table lookup).  Slots past n hold +inf and a zero
+// step (set by the host), so all slots are compared.
 __device__ inline uint32_t bits_of(uint16_t xh, const AssignRegs& r) {
   const float ax = __builtin_fabsf(half_bits_to_float(xh));
-  uint32_t b = r.lv[0];
+  int b = r.lv0;
 #pragma unroll
-  for (int t = 0; t < kMaxThresholds; ++t) b = (t < r.n && ax >= r.th[t]) ? r.lv[t + 1] : b;
-  return b;
+  for (int t = 0; t < kMaxThresholds; ++t) b += ax >= r.th[t] ? r.step[t] : 0;
+  return (uint32_t)b;
 }
 
 // Host-side status plumbing (api.hip).

@@ -201,18 +201,21 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
   __shared__ int s_last;
 
   const AssignRegs ar = load_assign_regs(a.ap);   // scalar registers, read before any global load
+  // workgroup = (column tile, 128-row group), tiles fastest (K, N < 2^31)
   const int tile = blockIdx.x % a.tiles;
   const int split = blockIdx.x / a.tiles;
-  const int64_t k0 = (int64_t)split * kRowsPerWG;
-  const int64_t k1 = (k0 + kRowsPerWG) < a.K ? (k0 + kRowsPerWG) : a.K;
-  const int64_t Np = padded_cols(a.N);
-  const int64_t t0 = (int64_t)tile * kTile;
-  const int ct = (int)((Np - t0) < kTile ? (Np - t0) : kTile);   // multiple of 128
+  const int K = (int)a.K, N = (int)a.N;
+  const int k0 = split * kRowsPerWG;
+  const int k1 = (k0 + kRowsPerWG) < K ? (k0 + kRowsPerWG) : K;
+  const int Np = (N + 127) & ~127;
+  const int t0 = tile * kTile;
+  const int ct = (Np - t0) < kTile ? (Np - t0) : kTile;   // multiple of 128
   const int pb = ct / 8;                                          // bytes per plane, multiple of 16
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int64_t g = split;
+
 
   // ---- every wave sees all rows of the group, two per lane (lane and lane
   // + 64): activation loads first, then scale and zero of this thread's two
@@ -229,25 +232,18 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
       rq[e] = lane + 64 * e;
     }
   }
+  // keep the activation loads ahead of the scale/zero loads: waits count
+  // loads in issue order, and the bits need only x
+  __builtin_amdgcn_sched_barrier(0);
   uint16_t sc[2], zr[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     int col = tid + u * kVmmThreads;
     col = col < ct ? col : ct - 1;
-    int64_t gc = t0 + col;
-    gc = gc < a.N ? gc : a.N - 1;
-    sc[u] = a.scales[g * a.N + gc];
-    zr[u] = a.zeros[g * a.N + gc];
-  }
-  if constexpr (kOut == kOutAccumulate) {
-    // the caller's next output buffer, zeroed once per column (split 0 only)
-    if (a.clear && split == 0) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int col = tid + u * kVmmThreads;
-        if (col < ct && t0 + col < a.N) a.clear[t0 + col] = 0.0f;
-      }
-    }
+    int gc = t0 + col;
+    gc = gc < N ? gc : N - 1;
+    sc[u] = a.scales[g * N + gc];
+    zr[u] = a.zeros[g * N + gc];
   }
 
   if constexpr (kFused) {
@@ -377,7 +373,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
 
   // buffer descriptor over this group's row tiles of the tile block
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.planes + t0 * a.K + k0 * ct), (short)0, (int)((k1 - k0) * ct), kRsrcWord3);
+      (void*)(a.planes + (int64_t)t0 * a.K + (int64_t)k0 * ct), (short)0, (k1 - k0) * ct, kRsrcWord3);
 
   float acc[32];
 #pragma unroll
@@ -430,7 +426,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int col = tid + u * kVmmThreads;
-    if (m > 0 && col < ct && t0 + col < a.N) {
+    if (m > 0 && col < ct && t0 + col < N) {
       float A = 0.0f;
 #pragma unroll
       for (int h = 0; h < kWaves; ++h) A += red[(h * 32 + (col >> 5)) * kRedStride + (col & 31)];
@@ -444,8 +440,16 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int col = tid + u * kVmmThreads;
-        if (col < ct && t0 + col < a.N)
+        if (col < ct && t0 + col < N)
           __hip_atomic_fetch_add(a.y + t0 + col, val[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    // the caller's next output buffer, zeroed once per column (split 0 only)
+    if (a.clear && split == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int col = tid + u * kVmmThreads;
+        if (col < ct && t0 + col < N) a.clear[t0 + col] = 0.0f;
       }
     }
     return;
@@ -454,7 +458,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int col = tid + u * kVmmThreads;
-        if (col < ct && t0 + col < a.N) a.y[t0 + col] = val[u];
+        if (col < ct && t0 + col < N) a.y[t0 + col] = val[u];
       }
       return;
     }
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int col = tid + e * kVmmThreads;
-      if (col < ct && t0 + col < a.N) a.y[t0 + col] = sum[e];
+      if (col < ct && t0 + col < N) a.y[t0 + col] = sum[e];
     }
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -514,6 +518,8 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
 
 static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_t s) {
   const VmmGeometry g = vmm_geometry(a.K, a.N);
+  if (g.splits * g.tiles > 0x7FFFFFFF)
+    return fail(GRINQH_EINVAL, "%lld workgroups: more than one launch handles", (long long)(g.splits * g.tiles));
   if (g.partial_floats * 4 >= (int64_t)kOutOfRange)
     return fail(GRINQH_EINVAL, "K x N too large for one split-K workspace (%lld partial floats)",
                 (long long)g.partial_floats);
