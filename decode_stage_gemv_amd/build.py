@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import glob
 import os
+import re
 import subprocess
 import sys
 
@@ -24,7 +25,24 @@ FLAGS = [
     "-Wno-unused-function",
     # Keep the compiler from emitting packed fp32 arithmetic.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Per-kernel register, scratch and occupancy report (checked below).
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+
+def resource_usage(stderr: str) -> dict:
+    """{kernel: {"VGPRs": n, "ScratchSize": n, "Occupancy": n}} from the compiler's remarks."""
+    usage, name = {}, None
+    for line in stderr.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            usage[name] = {}
+            continue
+        m = re.search(r"remark:\s+(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and name:
+            usage[name][m.group(1).split()[0]] = int(m.group(2))
+    return usage
 
 
 def sources():
@@ -42,6 +60,20 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libgrinqh.so")
+    usage = resource_usage(res.stderr)
+    if not usage:
+        raise RuntimeError("no kernel resource report from hipcc")
+    # No kernel may spill to scratch (private memory): it turns register
+    # arrays into slow memory round trips.  The VMM kernels must keep four
+    # waves per SIMD (two 512-thread workgroups per CU).
+    for name, u in usage.items():
+        if u.get("ScratchSize", 0) != 0:
+            raise RuntimeError(f"{name} uses {u['ScratchSize']} bytes of scratch per lane")
+        if "vmm_kernel" in name and u.get("Occupancy", 0) < 4:
+            raise RuntimeError(f"{name}: occupancy {u.get('Occupancy')} waves/SIMD, expected >= 4")
+    if verbose:
+        for name, u in sorted(usage.items()):
+            print(f"  {name}: {u}")
     os.replace(tmp, LIB)
     return LIB
 
