@@ -192,30 +192,27 @@ enum : int {
   kOutAccumulate = 1  // fp32 device-scope atomic adds into y (y += x W)
 };
 
+// The activation pointer, K and the tile count come first as plain scalars:
+// the build asks for them to be preloaded into scalar registers, so the
+// activation loads can issue before the rest of the arguments arrive.
 template <bool kFused, int kOut>
-__global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
+__global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __restrict__ x, int K, int tiles,
+                                                          VmmArgs a) {
   __shared__ float s_red[kRedWords];                      // wave reduction
   __shared__ uint32_t s_src[kWaves][kMaxRecords * 4];     // per wave: record row -> source byte offset
   __shared__ uint32_t s_cx[kWaves][kMaxRecords * 2];      // per wave: record pair -> fp16 x of its rows
   __shared__ float s_hx[2];
   __shared__ int s_last;
 
-  const AssignRegs ar = load_assign_regs(a.ap);   // scalar registers, read before any global load
   // workgroup = (column tile, 128-row group), tiles fastest (K, N < 2^31)
-  const int tile = blockIdx.x % a.tiles;
-  const int split = blockIdx.x / a.tiles;
-  const int K = (int)a.K, N = (int)a.N;
+  const int tile = blockIdx.x % tiles;
+  const int split = blockIdx.x / tiles;
   const int k0 = split * kRowsPerWG;
   const int k1 = (k0 + kRowsPerWG) < K ? (k0 + kRowsPerWG) : K;
-  const int Np = (N + 127) & ~127;
-  const int t0 = tile * kTile;
-  const int ct = (Np - t0) < kTile ? (Np - t0) : kTile;   // multiple of 128
-  const int pb = ct / 8;                                          // bytes per plane, multiple of 16
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int64_t g = split;
-
 
   // ---- every wave sees all rows of the group, two per lane (lane and lane
   // + 64): activation loads first, then scale and zero of this thread's two
@@ -228,13 +225,19 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int64_t i = k0 + lane + 64 * e;
-      xq[e] = a.x[i < k1 ? i : k1 - 1];
+      xq[e] = x[i < k1 ? i : k1 - 1];
       rq[e] = lane + 64 * e;
     }
   }
-  // keep the activation loads ahead of the scale/zero loads: waits count
-  // loads in issue order, and the bits need only x
+  // keep the activation loads ahead of everything else: they need only the
+  // preloaded arguments, and waits count loads in issue order
   __builtin_amdgcn_sched_barrier(0);
+  const AssignRegs ar = load_assign_regs(a.ap);   // scalar registers
+  const int N = (int)a.N;
+  const int Np = (N + 127) & ~127;
+  const int t0 = tile * kTile;
+  const int ct = (Np - t0) < kTile ? (Np - t0) : kTile;   // multiple of 128
+  const int pb = ct / 8;                                  // bytes per plane, multiple of 16
   uint16_t sc[2], zr[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(VmmArgs a) {
           rq[e] = (int)(i - k0);
           uint32_t bb = a.bits[i];
           bq[e] = bb > 8u ? 8u : bb;
-          xq[e] = a.x[i];
+          xq[e] = x[i];
         }
       }
     }
@@ -531,14 +534,14 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_
   const dim3 block(kVmmThreads);
   if (out_mode == kOutAccumulate) {
     if (fused)
-      hipLaunchKernelGGL((vmm_kernel<true, kOutAccumulate>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((vmm_kernel<true, kOutAccumulate>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
     else
-      hipLaunchKernelGGL((vmm_kernel<false, kOutAccumulate>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((vmm_kernel<false, kOutAccumulate>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
   } else {
     if (fused)
-      hipLaunchKernelGGL((vmm_kernel<true, kOutSplitK>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((vmm_kernel<true, kOutSplitK>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
     else
-      hipLaunchKernelGGL((vmm_kernel<false, kOutSplitK>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((vmm_kernel<false, kOutSplitK>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
   }
   return check_launch(out_mode == kOutAccumulate ? "grinqh_decode_vmm_accumulate"
                                                  : (fused ? "grinqh_decode_vmm" : "grinqh_vmm"));
