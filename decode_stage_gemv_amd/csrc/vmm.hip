@@ -15,11 +15,13 @@
 // order).
 //
 // Loads.  A lane loads its pair's plane words straight into registers with
-// 4-byte buffer loads: planes p < b come from the row tile, planes p >= b use
-// an out-of-range scalar offset, which returns 0 and moves no bytes, so only
-// the top b planes of a row are fetched.  Three records are in flight per
-// wave; a wave waits only for its own loads and never for
-// another wave until the final reduction.
+// 4-byte buffer loads: planes p < b come from the row tile; the loads of
+// planes p >= b repeat plane 0 (a cache hit that the width-specialised
+// rebuild ignores) so that every record is the same 16 loads; padding rows
+// use an out-of-range voffset, which returns 0 and moves no bytes.  Only the
+// top b planes of a row are fetched from memory.  Three records are in
+// flight per wave; a wave waits only for its own loads and never for another
+// wave until the final reduction.
 //
 // Compute.  The codes come back from the planes through a bit-transpose
 // network (bitplane.hpp); byte j of code word m from the two rows of a pair
