@@ -65,7 +65,8 @@ int check_launch(const char* what);
 
 // Workspace geometry used by the VMM kernels and grinqh_workspace_bytes.
 struct VmmGeometry {
-  int64_t rows_per_split;  // K rows handled by one workgroup
+  int64_t rows_per_split;  // K rows handled by one workgroup (64 or 128)
+  int64_t waves;           // waves per workgroup (4 or 8)
   int64_t splits;          // ceil(K / rows_per_split)
   int64_t tiles;           // column tiles
   int64_t partial_floats;  // splits * N_pad when splits > 1, else 0

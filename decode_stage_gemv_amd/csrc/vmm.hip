@@ -42,13 +42,15 @@
 
 namespace grinqh {
 
-constexpr int kVmmThreads = 512;                 // 8 waves
-constexpr int kWaves = kVmmThreads / 64;
-constexpr int kRowsPerWG = kGroup;               // one scale group per workgroup
-constexpr int kMaxCouples = kRowsPerWG / 4 + 6;  // sum over 8 widths of ceil(c_v / 4) <= (128 + 8 * 3) / 4
-constexpr int kMaxRecords = (kMaxCouples + kWaves - 1) / kWaves;
+constexpr int kMaxRows = kGroup;                 // rows of one workgroup: 128 or 64, within one scale group
+constexpr int kMaxCouples = kMaxRows / 4 + 6;    // sum over 8 widths of ceil(c_v / 4) <= (128 + 8 * 3) / 4
 constexpr int kRedStride = 33;                   // LDS row stride of the wave reduction
-constexpr int kRedWords = kWaves * 32 * kRedStride;
+// Launch shape.  The grid is (row item, column tile) pairs.  Small layers
+// use 64-row items so that more workgroups share the CUs; layers that need
+// more than one round of workgroups use 4-wave workgroups (more of them
+// resident per CU, so one's prologue overlaps another's streaming), the
+// others 8-wave workgroups.
+constexpr int kTargetCUs = 256;                  // MI355X
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;    // buffer offset beyond any range used here
 constexpr int kRsrcWord3 = 0x00020000;           // raw 32-bit buffer, gfx9 family
 constexpr int kScopeDevice = 16;                 // cache-policy bits: sc1 = device scope
@@ -60,9 +62,10 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 VmmGeometry vmm_geometry(int64_t K, int64_t N) {
   VmmGeometry g;
-  g.rows_per_split = kRowsPerWG;
-  g.splits = (K + kRowsPerWG - 1) / kRowsPerWG;
   g.tiles = n_tiles(N);
+  g.rows_per_split = n_groups(K) * g.tiles < kTargetCUs ? 64 : 128;
+  g.splits = (K + g.rows_per_split - 1) / g.rows_per_split;
+  g.waves = g.splits * g.tiles > 2 * kTargetCUs ? 4 : 8;
   g.partial_floats = g.splits > 1 ? g.splits * padded_cols(N) : 0;
   g.counter_offset = (g.partial_floats * 4 + 255) / 256 * 256;
   g.bytes = g.splits > 1 ? g.counter_offset + g.tiles * 4 : 0;
@@ -82,7 +85,7 @@ struct VmmArgs {
   float* partials;
   unsigned* counters;
   int64_t K, N;
-  int splits, tiles;
+  int splits, tiles, rows;
   AssignParams ap;
 };
 
@@ -148,6 +151,7 @@ struct RecordRegs {
 // plane 0 (a cache hit; compute_record ignores them), and a padding row or a
 // record the wave does not have uses an out-of-range voffset, which returns
 // 0 and moves no bytes (only the voffset takes part in the range check).
+template <int kMaxRecords>
 __device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, const uint32_t* src,
                                    int j, int b, int pb) {
   const int h = (threadIdx.x >> 5) & 1;
@@ -197,9 +201,13 @@ enum : int {
 // The activation pointer, K and the tile count come first as plain scalars:
 // the build asks for them to be preloaded into scalar registers, so the
 // activation loads can issue before the rest of the arguments arrive.
-template <bool kFused, int kOut>
-__global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __restrict__ x, int K, int tiles,
+template <bool kFused, int kOut, int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __restrict__ x, int K, int tiles,
                                                           VmmArgs a) {
+  constexpr int kVmmThreads = 64 * kWaves;
+  constexpr int kCols = kTile / kVmmThreads;        // output columns per thread in the epilogue
+  constexpr int kMaxRecords = (kMaxCouples + kWaves - 1) / kWaves;
+  constexpr int kRedWords = kWaves * 32 * kRedStride;
   __shared__ float s_red[kRedWords];                      // wave reduction
   __shared__ uint32_t s_src[kWaves][kMaxRecords * 4];     // per wave: record row -> source byte offset
   __shared__ uint32_t s_cx[kWaves][kMaxRecords * 2];      // per wave: record pair -> fp16 x of its rows
@@ -209,12 +217,12 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
   // workgroup = (column tile, 128-row group), tiles fastest (K, N < 2^31)
   const int tile = blockIdx.x % tiles;
   const int split = blockIdx.x / tiles;
-  const int k0 = split * kRowsPerWG;
-  const int k1 = (k0 + kRowsPerWG) < K ? (k0 + kRowsPerWG) : K;
+  const int k0 = split * a.rows;
+  const int k1 = (k0 + a.rows) < K ? (k0 + a.rows) : K;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int64_t g = split;
+  const int64_t g = k0 / kGroup;                // scale group
 
   // ---- every wave sees all rows of the group, two per lane (lane and lane
   // + 64): activation loads first, then scale and zero of this thread's two
@@ -240,9 +248,9 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
   const int t0 = tile * kTile;
   const int ct = (Np - t0) < kTile ? (Np - t0) : kTile;   // multiple of 128
   const int pb = ct / 8;                                  // bytes per plane, multiple of 16
-  uint16_t sc[2], zr[2];
+  uint16_t sc[kCols], zr[kCols];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kCols; ++u) {
     int col = tid + u * kVmmThreads;
     col = col < ct ? col : ct - 1;
     int gc = t0 + col;
@@ -263,7 +271,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
       const int64_t p0 = wave_lower_bound(a.active_idx, n, k0);
       const int64_t p1 = wave_lower_bound(a.active_idx, n, k1);
       int m = (int)(p1 - p0);
-      m = m < 0 ? 0 : (m > kRowsPerWG ? kRowsPerWG : m);
+      m = m < 0 ? 0 : (m > kMaxRows ? kMaxRows : m);
       if (lane == 0) {
         s_m = m;
         s_p0 = (int)p0;
@@ -399,14 +407,14 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       bw[j] = width(j);
-      load_record(rr[j], rsrc, src, j, bw[j], pb);
+      load_record<kMaxRecords>(rr[j], rsrc, src, j, bw[j], pb);
     }
 #pragma unroll
     for (int j = 0; j < kMaxRecords; ++j) {
       if (j < nrec) compute_record(rr[j % 3], bw[j % 3], cx[2 * j + h], acc);
       if (j + 3 < kMaxRecords) {
         bw[j % 3] = width(j + 3);
-        load_record(rr[j % 3], rsrc, src, j + 3, bw[j % 3], pb);
+        load_record<kMaxRecords>(rr[j % 3], rsrc, src, j + 3, bw[j % 3], pb);
       }
     }
   }
@@ -427,9 +435,10 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
   __syncthreads();
   const float H = s_hx[0];
   const float X = s_hx[1];
-  float val[2] = {0.0f, 0.0f};
+  float val[kCols];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kCols; ++u) {
+    val[u] = 0.0f;
     const int col = tid + u * kVmmThreads;
     if (m > 0 && col < ct && t0 + col < N) {
       float A = 0.0f;
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
   if constexpr (kOut == kOutAccumulate) {
     if (m > 0) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kCols; ++u) {
         const int col = tid + u * kVmmThreads;
         if (col < ct && t0 + col < N)
           __hip_atomic_fetch_add(a.y + t0 + col, val[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -452,7 +461,7 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
     // the caller's next output buffer, zeroed once per column (split 0 only)
     if (a.clear && split == 0) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kCols; ++u) {
         const int col = tid + u * kVmmThreads;
         if (col < ct && t0 + col < N) a.clear[t0 + col] = 0.0f;
       }
@@ -461,14 +470,14 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
   } else {
     if (a.splits == 1) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kCols; ++u) {
         const int col = tid + u * kVmmThreads;
         if (col < ct && t0 + col < N) a.y[t0 + col] = val[u];
       }
       return;
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < kCols; ++u) {
       const int col = tid + u * kVmmThreads;
       // device-scope store: written through to the point where every XCD sees it
       if (col < ct)
@@ -492,32 +501,51 @@ __global__ __launch_bounds__(kVmmThreads) void vmm_kernel(const uint16_t* __rest
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.partials + t0), (short)0, (int)(a.splits * Np * 4), (int)kRsrcWord3);
     const uint32_t row_bytes = (uint32_t)(Np * 4);
-    float sum[2] = {0.0f, 0.0f};
-    // 32 splits per round, all loads of a round in flight together; splits
-    // past the end read as zero (out-of-range offsets)
-    for (int sp0 = 0; sp0 < a.splits; sp0 += 32) {
-      uint32_t v[32][2];
+    float sum[kCols];
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
+    for (int e = 0; e < kCols; ++e) sum[e] = 0.0f;
+    constexpr int kRound = 64 / kCols;   // splits per round (loads in flight per thread: 64)
+    // kRound splits per round, all loads of a round in flight together;
+    // splits past the end read as zero (out-of-range offsets); the sum runs
+    // in split order
+    for (int sp0 = 0; sp0 < a.splits; sp0 += kRound) {
+      uint32_t v[kRound][kCols];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+      for (int u = 0; u < kRound; ++u)
+#pragma unroll
+        for (int e = 0; e < kCols; ++e) {
           const int col = tid + e * kVmmThreads;
           const bool ok = sp0 + u < a.splits && col < ct;
           const uint32_t off = ok ? (uint32_t)(sp0 + u) * row_bytes + 4u * (uint32_t)col : kOutOfRange;
           v[u][e] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, kScopeDevice);
         }
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        sum[0] += __builtin_bit_cast(float, v[u][0]);
-        sum[1] += __builtin_bit_cast(float, v[u][1]);
-      }
+      for (int u = 0; u < kRound; ++u)
+#pragma unroll
+        for (int e = 0; e < kCols; ++e) sum[e] += __builtin_bit_cast(float, v[u][e]);
     }
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < kCols; ++e) {
       const int col = tid + e * kVmmThreads;
       if (col < ct && t0 + col < N) a.y[t0 + col] = sum[e];
     }
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int kWaves>
+static void launch_shape(bool fused, int out_mode, dim3 grid, const VmmArgs& a, hipStream_t s) {
+  const dim3 block(64 * kWaves);
+  if (out_mode == kOutAccumulate) {
+    if (fused)
+      hipLaunchKernelGGL((vmm_kernel<true, kOutAccumulate, kWaves>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
+    else
+      hipLaunchKernelGGL((vmm_kernel<false, kOutAccumulate, kWaves>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((vmm_kernel<true, kOutSplitK, kWaves>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
+    else
+      hipLaunchKernelGGL((vmm_kernel<false, kOutSplitK, kWaves>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
   }
 }
 
@@ -530,21 +558,14 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_
                 (long long)g.partial_floats);
   a.splits = (int)g.splits;
   a.tiles = (int)g.tiles;
+  a.rows = (int)g.rows_per_split;
   a.partials = reinterpret_cast<float*>(ws);
   a.counters = g.bytes > 0 && ws ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + g.counter_offset) : nullptr;
   const dim3 grid((unsigned)(g.splits * g.tiles));
-  const dim3 block(kVmmThreads);
-  if (out_mode == kOutAccumulate) {
-    if (fused)
-      hipLaunchKernelGGL((vmm_kernel<true, kOutAccumulate>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
-    else
-      hipLaunchKernelGGL((vmm_kernel<false, kOutAccumulate>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
-  } else {
-    if (fused)
-      hipLaunchKernelGGL((vmm_kernel<true, kOutSplitK>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
-    else
-      hipLaunchKernelGGL((vmm_kernel<false, kOutSplitK>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
-  }
+  if (g.waves == 4)
+    launch_shape<4>(fused, out_mode, grid, a, s);
+  else
+    launch_shape<8>(fused, out_mode, grid, a, s);
   return check_launch(out_mode == kOutAccumulate ? "grinqh_decode_vmm_accumulate"
                                                  : (fused ? "grinqh_decode_vmm" : "grinqh_vmm"));
 }
