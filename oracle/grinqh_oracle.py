@@ -10,9 +10,10 @@ Generation" (arXiv 2606.23419).  Each function names the section or equation
 it follows.  Where the paper is silent the plainest reading is taken; each
 such reading is marked "Reading:" below.
 
-Notation: K input rows (d_in), N output columns (d_out), b_max = 8, groups of
-128 rows share one (scale, zero) pair per column, x is the fp16 activation of
-the current token.
+Notation: K input rows (d_in), N output columns (d_out), b_max the bit width
+of the stored codes (8 unless a function is told otherwise; section 3.3
+evaluates b_max in {4, 6, 8}), groups of 128 rows share one (scale, zero) pair
+per column, x is the fp16 activation of the current token.
 """
 from __future__ import annotations
 
@@ -152,58 +153,75 @@ def tiles(N: int):
     return [(t0, min(TILE, Np - t0)) for t0 in range(0, Np, TILE)]
 
 
-def planes_bytes(K: int, N: int) -> int:
-    return K * padded_cols(N)
+def _check_bmax(b_max: int) -> int:
+    b_max = int(b_max)
+    if not 1 <= b_max <= 8:
+        raise ValueError(f"b_max = {b_max}, expected 1..8")
+    return b_max
 
 
-def plane_offset(K: int, N: int, t: int, i: int, p: int) -> int:
+def planes_bytes(K: int, N: int, b_max: int = B_MAX) -> int:
+    """Store size: b_max planes of N_pad / 8 bytes per row."""
+    return K * padded_cols(N) * _check_bmax(b_max) // 8
+
+
+def plane_offset(K: int, N: int, t: int, i: int, p: int, b_max: int = B_MAX) -> int:
     """Byte offset of plane p (0 = most significant) of row i in tile t.
 
-    Tile t is a block of K row tiles; a row tile holds its 8 planes back to
-    back, C_t / 8 bytes each, so planes 0..b-1 form one contiguous span.
+    Tile t is a block of K row tiles; a row tile holds its b_max planes back
+    to back, C_t / 8 bytes each, so planes 0..b-1 form one contiguous span.
+    A b_max-bit store is the 8-bit one with fewer planes per row (section 3.3:
+    the same format for any maximum width; Appendix C.1: a smaller b_max just
+    stops earlier).
     """
+    b_max = _check_bmax(b_max)
     t0, ct = tiles(N)[t]
-    return t * K * TILE + i * ct + p * (ct // 8)
+    return (t * K * TILE + i * ct) * b_max // 8 + p * (ct // 8)
 
 
-def pack(codes: np.ndarray) -> np.ndarray:
-    """8-bit codes [K][N] -> MSB-first bit planes (the store above).
+def pack(codes: np.ndarray, b_max: int = B_MAX) -> np.ndarray:
+    """b_max-bit codes [K][N] -> MSB-first bit planes (the store above).
 
-    Within a plane, 32 consecutive columns form one little-endian 32-bit word.
-    Column 32w + 4m + j (m = 0..7, j = 0..3) of the word sits at bit 8j + m,
-    so byte j of a plane word holds the plane bits of columns j, 4+j, ..., 28+j.
-    (The paper groups and permutes packed bits offline so that the kernel
-    rebuilds codes with OR and SHIFT only, Appendix C.1 "Grouping"; this is
-    this project's permutation for 1-bit planes.)  Padding columns N..N_pad-1
-    hold code 0.
+    Plane p holds bit (b_max - 1 - p) of the code.  Within a plane, 32
+    consecutive columns form one little-endian 32-bit word.  Column
+    32w + 4m + j (m = 0..7, j = 0..3) of the word sits at bit 8j + m, so byte j
+    of a plane word holds the plane bits of columns j, 4+j, ..., 28+j.  (The
+    paper groups and permutes packed bits offline so that the kernel rebuilds
+    codes with OR and SHIFT only, Appendix C.1 "Grouping"; this is this
+    project's permutation for 1-bit planes.)  Padding columns N..N_pad-1 hold
+    code 0.  Codes must lie in [0, 2^b_max).
     """
+    b_max = _check_bmax(b_max)
     codes = np.asarray(codes, dtype=np.uint8)
+    if codes.size and int(codes.max()) >= (1 << b_max):
+        raise ValueError(f"a code exceeds {b_max} bits")
     K, N = codes.shape
     Np = padded_cols(N)
     q = np.zeros((K, Np), dtype=np.uint8)
     q[:, :N] = codes
-    out = np.zeros(planes_bytes(K, N), dtype=np.uint8)
+    out = np.zeros(planes_bytes(K, N, b_max), dtype=np.uint8)
     for t, (t0, ct) in enumerate(tiles(N)):
         W = ct // WORD
         sub = q[:, t0:t0 + ct].reshape(K, W, 8, 4)          # [i][w][m][j]
-        block = np.empty((K, 8, ct // 8), dtype=np.uint8)
-        for p in range(8):
-            bit = (sub >> (7 - p)) & 1                        # plane p = bit 7-p
+        block = np.empty((K, b_max, ct // 8), dtype=np.uint8)
+        for p in range(b_max):
+            bit = (sub >> (b_max - 1 - p)) & 1                # plane p = bit b_max-1-p
             bit = np.ascontiguousarray(bit.transpose(0, 1, 3, 2))   # [i][w][j][m]
             by = np.packbits(bit, axis=-1, bitorder="little")       # byte j, bit m
             block[:, p, :] = by.reshape(K, W * 4)
-        base = t * K * TILE
-        out[base:base + K * ct] = block.reshape(-1)
+        base = plane_offset(K, N, t, 0, 0, b_max)
+        out[base:base + block.size] = block.reshape(-1)
     return out
 
 
-def read_planes(planes: np.ndarray, K: int, N: int, bits: np.ndarray) -> np.ndarray:
+def read_planes(planes: np.ndarray, K: int, N: int, bits: np.ndarray, b_max: int = B_MAX) -> np.ndarray:
     """Codes as seen through the store: the top b_i planes of row i.
 
-    Returns u8 [K][N] holding q_b * 2^(8 - b) (the b-bit prefix of the code in
-    its original bit positions, low bits zero).  Reads only the planes a row
-    needs (section 3.3: load the most significant segments only).
+    Returns u8 [K][N] holding q_b * 2^(b_max - b) (the b-bit prefix of the
+    code in its original bit positions, low bits zero).  Reads only the planes
+    a row needs (section 3.3: load the most significant segments only).
     """
+    b_max = _check_bmax(b_max)
     planes = np.asarray(planes, dtype=np.uint8)
     bits = np.asarray(bits)
     out = np.zeros((K, padded_cols(N)), dtype=np.uint8)
@@ -211,14 +229,16 @@ def read_planes(planes: np.ndarray, K: int, N: int, bits: np.ndarray) -> np.ndar
         W = ct // WORD
         for i in range(K):
             b = int(bits[i])
-            start = plane_offset(K, N, t, i, 0)
+            if b > b_max:
+                raise ValueError(f"row {i}: {b} bits from a {b_max}-bit store")
+            start = plane_offset(K, N, t, i, 0, b_max)
             span = planes[start:start + b * (ct // 8)]
             acc = np.zeros(ct, dtype=np.uint8)
             for p in range(b):
                 by = span[p * (ct // 8):(p + 1) * (ct // 8)].reshape(W, 4, 1)
                 bit = np.unpackbits(by, axis=-1, bitorder="little")      # [w][j][m]
                 bit = bit.transpose(0, 2, 1).reshape(ct)                 # col 32w+4m+j
-                acc |= (bit << (7 - p)).astype(np.uint8)
+                acc |= (bit << (b_max - 1 - p)).astype(np.uint8)
             out[i, t0:t0 + ct] = acc
     return out[:, :N]
 
@@ -234,37 +254,40 @@ def span_bytes(K: int, N: int, bits: np.ndarray) -> int:
 # and Bias Correction".
 # --------------------------------------------------------------------------
 
-def reconstruct_level(q: np.ndarray, b: int) -> np.ndarray:
-    """q_b 2^(b_max - b) + phi for codes q at bit width b, as fp64.
+def reconstruct_level(q: np.ndarray, b: int, b_max: int = B_MAX) -> np.ndarray:
+    """q_b 2^(b_max - b) + phi for b_max-bit codes q at bit width b, as fp64.
 
-    q_b = floor(q / 2^(8 - b)) is the truncated code and phi = 2^(8 - b - 1)
-    the midpoint correction (section 3.3).  Reading: at b = b_max nothing is
-    truncated and phi = 0, so the full code is used as is.
+    q_b = floor(q / 2^(b_max - b)) is the truncated code and
+    phi = 2^(b_max - b - 1) the midpoint correction (section 3.3).  Reading: at
+    b = b_max nothing is truncated and phi = 0, so the full code is used as is.
     """
-    step = float(2 ** (B_MAX - b))
+    b_max = _check_bmax(b_max)
+    if not 0 <= b <= b_max:
+        raise ValueError(f"bit width {b} outside 0..{b_max}")
+    step = float(2 ** (b_max - b))
     qb = np.floor(np.asarray(q, dtype=np.float64) / step)
-    phi = float(2 ** (B_MAX - b - 1)) if b < B_MAX else 0.0
+    phi = float(2 ** (b_max - b - 1)) if b < b_max else 0.0
     return qb * step + phi
 
 
-def _dequant_rows(codes, scales, zeros, rows, bits):
-    """w_hat = s (q_b 2^(8-b) + phi) + z for the given rows, fp64 [len(rows)][N]."""
+def _dequant_rows(codes, scales, zeros, rows, bits, b_max):
+    """w_hat = s (q_b 2^(b_max-b) + phi) + z for the given rows, fp64 [len(rows)][N]."""
     out = np.empty((len(rows), codes.shape[1]), dtype=np.float64)
     for r, i in enumerate(rows):
         b = int(bits[i])
         g = i // GROUP
         s = scales[g].astype(np.float64)
         z = zeros[g].astype(np.float64)
-        out[r] = s * reconstruct_level(codes[i], b) + z
+        out[r] = s * reconstruct_level(codes[i], b, b_max) + z
     return out
 
 
-def vmm(codes, scales, zeros, x, bits, chunk: int = 256) -> np.ndarray:
+def vmm(codes, scales, zeros, x, bits, chunk: int = 256, b_max: int = B_MAX) -> np.ndarray:
     """y_j = sum over rows with b_i > 0 of x_i * w_hat_ij, in fp64.
 
     Rows with b_i = 0 contribute nothing (bypassed, sections 2 and 3), which
     is the reading taken for "0-bit".  x, s and z enter as their exact fp16
-    values.  Returns fp64 [N].
+    values; codes are b_max-bit integers.  Returns fp64 [N].
     """
     codes = np.asarray(codes, dtype=np.uint8)
     K, N = codes.shape
@@ -273,12 +296,12 @@ def vmm(codes, scales, zeros, x, bits, chunk: int = 256) -> np.ndarray:
     y = np.zeros(N, dtype=np.float64)
     for c0 in range(0, len(rows), chunk):
         rr = rows[c0:c0 + chunk]
-        w_hat = _dequant_rows(codes, scales, zeros, rr, bits)
+        w_hat = _dequant_rows(codes, scales, zeros, rr, bits, b_max)
         y += x64[rr] @ w_hat
     return y
 
 
-def vmm_abs(codes, scales, zeros, x, bits, chunk: int = 256) -> np.ndarray:
+def vmm_abs(codes, scales, zeros, x, bits, chunk: int = 256, b_max: int = B_MAX) -> np.ndarray:
     """sum_i |x_i * w_hat_ij| over rows with b_i > 0 (the tolerance scale)."""
     codes = np.asarray(codes, dtype=np.uint8)
     K, N = codes.shape
@@ -287,16 +310,16 @@ def vmm_abs(codes, scales, zeros, x, bits, chunk: int = 256) -> np.ndarray:
     out = np.zeros(N, dtype=np.float64)
     for c0 in range(0, len(rows), chunk):
         rr = rows[c0:c0 + chunk]
-        w_hat = _dequant_rows(codes, scales, zeros, rr, bits)
+        w_hat = _dequant_rows(codes, scales, zeros, rr, bits, b_max)
         out += x64[rr] @ np.abs(w_hat)
     return out
 
 
-def decode_step(codes, scales, zeros, x, thresholds, levels):
+def decode_step(codes, scales, zeros, x, thresholds, levels, b_max: int = B_MAX):
     """One decode-stage VMM: assign, select active rows, multiply."""
     bits = assign(x, thresholds, levels)
     idx, m = compact(bits)
-    y = vmm(codes, scales, zeros, x, bits)
+    y = vmm(codes, scales, zeros, x, bits, b_max=b_max)
     return bits, idx, y
 
 

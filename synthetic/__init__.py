@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the GRINQH decode-stage vector-matrix multiply.
 
-This module only *draws* inputs: weight matrices already quantised to 8-bit
-asymmetric codes with per-(128-row group, column) fp16 scale and zero, fp16
+This module only *draws* inputs: weight matrices already quantised to b_max-bit
+(8 unless asked otherwise) asymmetric codes with per-(128-row group, column) fp16 scale and zero, fp16
 activation vectors, and the precision distributions P that the workloads use.
 It holds none of the GRINQH method's arithmetic (no threshold calibration, no
 precision assignment, no bit planes, no reconstruction).  Both the fp64 oracle
@@ -14,9 +14,11 @@ only the model shapes):
 * Weights ``W ~ N(0, 0.02^2)`` in fp32, quantised round-to-nearest at 8 bits,
   one (scale, zero) pair per group of 128 input rows and per output column, as
   in the RTN base the paper builds on ("Models and Baselines", section 4, group
-  size G = 128).  ``s = (max - min) / 255`` and ``z = min`` are rounded
-  round-to-nearest-even to fp16, and codes use those rounded values:
-  ``q = clip(rint((w - z) / s), 0, 255)`` (``q = 0`` where ``s == 0``).
+  size G = 128).  With L = 2^b_max - 1, ``s = (max - min) / L`` and
+  ``z = min`` are rounded round-to-nearest-even to fp16, and codes use those
+  rounded values: ``q = clip(rint((w - z) / s), 0, L)`` (``q = 0`` where
+  ``s == 0``).  b_max = 4 and 6 quantise the parent model at that width
+  directly, as section 3.3 asks of a store with a smaller maximum width.
   The base quantiser is an input recipe: the paper treats the quantisation
   step as independent of GRINQH (Appendix D.1).
 * Activations: ``|x_i| = exp(N(0, 1))`` with a random sign; a fixed set of
@@ -46,6 +48,11 @@ ROLE_W, ROLE_OUTLIERS, ROLE_CALIB, ROLE_TEST = 0, 1, 2, 3
 # below sums to 1 and its weighted average bit width is the key of the entry.
 LEVELS_5 = (0, 2, 3, 4, 8)
 LEVELS_4 = (0, 2, 4, 8)
+# Stores with a smaller maximum width (section 3.3 evaluates b_max in
+# {4, 6, 8}; Table 7 runs an effective 4 bits under b_max = 6 and an effective
+# 3 bits under b_max = 4), with 2-bit steps as in Figure 2.
+LEVELS_BMAX6 = (0, 2, 4, 6)
+LEVELS_BMAX4 = (0, 2, 4)
 
 P_LEVELS_5 = {
     2: (0.35, 0.30, 0.20, 0.10, 0.05),
@@ -79,6 +86,15 @@ QWEN3_8B_LAYERS = 36
 LLAMA3_70B_MLP = {"gate": (8192, 28672), "down": (28672, 8192)}
 
 
+P_BMAX6 = {
+    3: (0.20, 0.30, 0.30, 0.20),
+    4: (0.10, 0.20, 0.30, 0.40),
+}
+P_BMAX4 = {
+    2: (0.25, 0.50, 0.25),
+    3: (0.10, 0.30, 0.60),
+}
+
 def rng(config: int, matrix: int, role: int) -> np.random.Generator:
     """Independent PCG64 stream for one (config, matrix, role) triple."""
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([config, matrix, role])))
@@ -88,12 +104,15 @@ def n_groups(K: int) -> int:
     return (K + GROUP - 1) // GROUP
 
 
-def rtn_quantize(w: np.ndarray):
-    """Round-to-nearest 8-bit asymmetric quantisation of fp32 ``w[K][N]``.
+def rtn_quantize(w: np.ndarray, b_max: int = 8):
+    """Round-to-nearest b_max-bit asymmetric quantisation of fp32 ``w[K][N]``.
 
     Returns ``(codes u8[K][N], scales f16[G][N], zeros f16[G][N])``.  The last
     group may hold fewer than 128 rows.
     """
+    if not 1 <= b_max <= 8:
+        raise ValueError(f"b_max = {b_max}, expected 1..8")
+    top = float((1 << b_max) - 1)
     K, N = w.shape
     G = n_groups(K)
     codes = np.empty((K, N), dtype=np.uint8)
@@ -103,21 +122,21 @@ def rtn_quantize(w: np.ndarray):
         blk = w[g * GROUP:(g + 1) * GROUP].astype(np.float64)
         lo = blk.min(axis=0)
         hi = blk.max(axis=0)
-        s16 = ((hi - lo) / 255.0).astype(np.float16)
+        s16 = ((hi - lo) / top).astype(np.float16)
         z16 = lo.astype(np.float16)
         s64 = s16.astype(np.float64)
         z64 = z16.astype(np.float64)
         with np.errstate(divide="ignore", invalid="ignore"):
             q = np.rint((blk - z64) / s64)
         q = np.where(s64 == 0.0, 0.0, q)
-        codes[g * GROUP:(g + 1) * GROUP] = np.clip(q, 0, 255).astype(np.uint8)
+        codes[g * GROUP:(g + 1) * GROUP] = np.clip(q, 0, top).astype(np.uint8)
         scales[g] = s16
         zeros[g] = z16
     return codes, scales, zeros
 
 
-def make_weights(K: int, N: int, config: int = 0, matrix: int = 0):
-    """Seeded ``W ~ N(0, 0.02^2)`` quantised by :func:`rtn_quantize`."""
+def make_weights(K: int, N: int, config: int = 0, matrix: int = 0, b_max: int = 8):
+    """Seeded ``W ~ N(0, 0.02^2)`` quantised by :func:`rtn_quantize` at b_max bits."""
     r = rng(config, matrix, ROLE_W)
     codes = np.empty((K, N), dtype=np.uint8)
     G = n_groups(K)
@@ -127,7 +146,7 @@ def make_weights(K: int, N: int, config: int = 0, matrix: int = 0):
     for g in range(G):
         rows = min(GROUP, K - g * GROUP)
         w = r.standard_normal((rows, N), dtype=np.float32) * np.float32(WEIGHT_STD)
-        c, s, z = rtn_quantize(w)
+        c, s, z = rtn_quantize(w, b_max)
         codes[g * GROUP:g * GROUP + rows] = c
         scales[g] = s[0]
         zeros[g] = z[0]
@@ -161,7 +180,7 @@ class Layer:
     """One linear layer's synthetic inputs."""
     K: int
     N: int
-    codes: np.ndarray      # u8 [K][N]
+    codes: np.ndarray      # u8 [K][N], b_max-bit values
     scales: np.ndarray     # f16 [G][N]
     zeros: np.ndarray      # f16 [G][N]
     calib: np.ndarray      # f16 [N_CALIB][K]
@@ -169,8 +188,8 @@ class Layer:
 
 
 def make_layer(K: int, N: int, config: int = 0, matrix: int = 0, n_test: int = 1,
-               n_calib: int = N_CALIB) -> Layer:
-    codes, scales, zeros = make_weights(K, N, config, matrix)
+               n_calib: int = N_CALIB, b_max: int = 8) -> Layer:
+    codes, scales, zeros = make_weights(K, N, config, matrix, b_max)
     calib = make_calibration(K, config, matrix, n_calib)
     x = make_activations(K, n_test, config, matrix, ROLE_TEST)
     return Layer(K, N, codes, scales, zeros, calib, x)

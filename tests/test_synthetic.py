@@ -40,6 +40,23 @@ def test_rtn_round_to_nearest_bound():
     assert q.min() == 0 and q.max() == 255
 
 
+@pytest.mark.parametrize("b_max", [4, 6])
+def test_rtn_bmax_bound(b_max):
+    """At b_max bits the codes span 0 .. 2^b_max - 1 and w_hat is within half a step."""
+    r = np.random.default_rng(b_max)
+    w = (r.standard_normal((260, 30)) * 0.02).astype(np.float32)
+    q, s, z = synthetic.rtn_quantize(w, b_max)
+    top = (1 << b_max) - 1
+    assert q.min() == 0 and q.max() == top
+    g = np.arange(260) // 128
+    s64 = s[g].astype(np.float64)
+    w_hat = s64 * q + z[g].astype(np.float64)
+    inside = (q > 0) & (q < top)
+    assert np.all(np.abs(w_hat - w)[inside] <= s64[inside] * 0.5 * (1 + 1e-9))
+    lay = synthetic.make_layer(200, 40, config=0, matrix=0, b_max=b_max)
+    assert lay.codes.max() <= top
+
+
 def test_outlier_channels():
     K = 4096
     x = synthetic.make_activations(K, 16, config=1, matrix=0).astype(np.float64)
@@ -50,7 +67,9 @@ def test_outlier_channels():
 
 
 @pytest.mark.parametrize("table,levels", [(synthetic.P_LEVELS_5, synthetic.LEVELS_5),
-                                          (synthetic.P_LEVELS_4, synthetic.LEVELS_4)])
+                                          (synthetic.P_LEVELS_4, synthetic.LEVELS_4),
+                                          (synthetic.P_BMAX6, synthetic.LEVELS_BMAX6),
+                                          (synthetic.P_BMAX4, synthetic.LEVELS_BMAX4)])
 def test_precision_tables(table, levels):
     for avg, P in table.items():
         assert sum(P) == pytest.approx(1.0, abs=1e-12)
