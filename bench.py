@@ -37,7 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 ROT_BYTES = 512 << 20
 
-# name: (K, N, config, matrix, P key, level set)
+# name: (K, N, config, matrix, P key, level set); level sets "b6" and "b4"
+# belong to stores of 6-bit and 4-bit codes (the others to 8-bit codes)
 WORKLOADS = {
     "llama3-8b-gate-4096x14336-avg3": (4096, 14336, 2, 4, 3, "5"),
     "llama3-8b-gate-4096x14336-avg2": (4096, 14336, 2, 4, 2, "5"),
@@ -52,10 +53,22 @@ WORKLOADS = {
 for _b in ("0.5", "1", "2", "3", "4", "6", "8"):
     WORKLOADS[f"llama3-70b-gate-8192x28672-avg{_b}"] = (8192, 28672, 4, 0, float(_b), "4")
     WORKLOADS[f"llama3-70b-down-28672x8192-avg{_b}"] = (28672, 8192, 4, 1, float(_b), "4")
+# smaller maximum widths: effective 3 and 4 bits under b_max = 6 and an
+# effective 2 and 3 bits under b_max = 4 (Table 7 runs 4-of-6 and 3-of-4)
+for _b in (3, 4):
+    WORKLOADS[f"llama3-8b-gate-4096x14336-bmax6-avg{_b}"] = (4096, 14336, 2, 4, _b, "b6")
+    WORKLOADS[f"llama3-70b-gate-8192x28672-bmax6-avg{_b}"] = (8192, 28672, 4, 0, _b, "b6")
+for _b in (2, 3):
+    WORKLOADS[f"llama3-8b-gate-4096x14336-bmax4-avg{_b}"] = (4096, 14336, 2, 4, _b, "b4")
+    WORKLOADS[f"llama3-70b-gate-8192x28672-bmax4-avg{_b}"] = (8192, 28672, 4, 0, _b, "b4")
 DEFAULT = "llama3-8b-gate-4096x14336-avg3"
 SWEEP = ([f"attn-proj-4096x4096-avg{b}" for b in (2, 3, 4, 8)]
          + [f"llama3-8b-gate-4096x14336-avg{b}" for b in (2, 3, 4, 8)]
          + [f"llama3-70b-gate-8192x28672-avg{b}" for b in ("0.5", "1", "2", "3", "4", "6", "8")])
+SWEEP_BMAX = ([f"llama3-8b-gate-4096x14336-bmax6-avg{b}" for b in (3, 4)]
+              + [f"llama3-8b-gate-4096x14336-bmax4-avg{b}" for b in (2, 3)]
+              + [f"llama3-70b-gate-8192x28672-bmax6-avg{b}" for b in (3, 4)]
+              + [f"llama3-70b-gate-8192x28672-bmax4-avg{b}" for b in (2, 3)])
 ENTRY = {"accumulate": "grinqh_decode_vmm_accumulate", "decode": "grinqh_decode_vmm"}
 TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "vmm_traffic_*.md")
 KERNEL_SOURCES = ("decode_stage_gemv_amd/csrc/vmm.hip", "decode_stage_gemv_amd/csrc/bitplane.hpp",
@@ -68,9 +81,16 @@ def log(msg):
 
 def _P(key, levels):
     import synthetic
-    table = synthetic.P_LEVELS_5 if levels == "5" else synthetic.P_LEVELS_4
-    lv = synthetic.LEVELS_5 if levels == "5" else synthetic.LEVELS_4
+    table, lv = {"5": (synthetic.P_LEVELS_5, synthetic.LEVELS_5),
+                 "4": (synthetic.P_LEVELS_4, synthetic.LEVELS_4),
+                 "b6": (synthetic.P_BMAX6, synthetic.LEVELS_BMAX6),
+                 "b4": (synthetic.P_BMAX4, synthetic.LEVELS_BMAX4)}[levels]
     return table[key], lv
+
+
+def bmax_of(levels):
+    """Code width of the store a level set belongs to."""
+    return {"b6": 6, "b4": 4}.get(levels, 8)
 
 
 def kernel_source_hash():
@@ -103,15 +123,15 @@ def measured_traffic(workload, mode):
 class Layer:
     """One synthetic layer packed on the GPU, in R rotated copies."""
 
-    def __init__(self, K, N, cfg, mat, copies_bytes=ROT_BYTES):
+    def __init__(self, K, N, cfg, mat, b_max=8, copies_bytes=ROT_BYTES):
         import torch
         import synthetic
         import decode_stage_gemv_amd as grq
         t0 = time.time()
-        self.K, self.N, self.cfg, self.mat = K, N, cfg, mat
-        lay = synthetic.make_layer(K, N, config=cfg, matrix=mat, n_test=1)
+        self.K, self.N, self.cfg, self.mat, self.b_max = K, N, cfg, mat, b_max
+        lay = synthetic.make_layer(K, N, config=cfg, matrix=mat, n_test=1, b_max=b_max)
         dev = torch.device("cuda:0")
-        planes = grq.pack(torch.from_numpy(lay.codes).to(dev))
+        planes = grq.pack(torch.from_numpy(lay.codes).to(dev), b_max=b_max)
         scales = torch.from_numpy(lay.scales).to(dev)
         zeros = torch.from_numpy(lay.zeros).to(dev)
         self.calib = torch.from_numpy(lay.calib).to(dev)
@@ -121,9 +141,9 @@ class Layer:
         self.copies = [(planes if r == 0 else planes.clone(), scales.clone(), zeros.clone(),
                         torch.from_numpy(self.xs_host[r]).to(dev)) for r in range(self.R)]
         self.host = lay
-        self.np_cols = int(grq.lib().grinqh_planes_bytes(1, N))
+        self.np_cols = int(grq.lib().grinqh_planes_bytes(1, N, 8))
         torch.cuda.synchronize()
-        log(f"layer {K}x{N}: R={self.R} copies, setup {time.time() - t0:.1f}s")
+        log(f"layer {K}x{N} (b_max {b_max}): R={self.R} copies, setup {time.time() - t0:.1f}s")
 
 
 class Prepared:
@@ -135,7 +155,9 @@ class Prepared:
         K, N, cfg, mat, pkey, lv = WORKLOADS[name]
         self.name, self.K, self.N, self.mode = name, K, N, mode
         self.P, self.levels = _P(pkey, lv)
-        self.layer = layer if layer is not None else Layer(K, N, cfg, mat)
+        self.b_max = bmax_of(lv)
+        self.layer = layer if layer is not None else Layer(K, N, cfg, mat, self.b_max)
+        assert self.layer.b_max == self.b_max
         self.R = self.layer.R
         self.thresholds = [float(v) for v in grq.calibrate(self.layer.calib, self.P).cpu().numpy()]
         dev = torch.device("cuda:0")
@@ -162,10 +184,11 @@ class Prepared:
         if self.mode == "accumulate":
             # decode-loop ping-pong: add into one buffer, clear the other for the next step
             grq.decode_vmm_accumulate(planes, scales, zeros, x, self.K, self.N, self.thresholds,
-                                      self.levels, self.ybufs[k % 2], self.ybufs[(k + 1) % 2])
+                                      self.levels, self.ybufs[k % 2], self.ybufs[(k + 1) % 2],
+                                      b_max=self.b_max)
         else:
             grq.decode_vmm(planes, scales, zeros, x, self.K, self.N, self.thresholds, self.levels,
-                           self.ws, out=self.y)
+                           self.ws, out=self.y, b_max=self.b_max)
 
     def run(self, steps, warmup, graph=True):
         """Time `steps` back-to-back steps; returns (ms per step, bytes per step).
@@ -240,7 +263,7 @@ def cpu_baseline(prep, budget_s=15.0):
     while t_total < budget_s and n < 50:
         x = prep.layer.xs_host[n % prep.R]
         t0 = time.perf_counter()
-        oracle.decode_step(lay.codes, lay.scales, lay.zeros, x, th, prep.levels)
+        oracle.decode_step(lay.codes, lay.scales, lay.zeros, x, th, prep.levels, b_max=prep.b_max)
         t_total += time.perf_counter() - t0
         bytes_total += prep.bytes[n % prep.R]
         n += 1
@@ -270,6 +293,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--sweep", action="store_true",
                     help="also time the bit-width sweep (4096^2, 4096x14336, 70B gate at 0.5..8 bits)")
+    ap.add_argument("--sweep-bmax", action="store_true",
+                    help="also time stores of 6-bit and 4-bit codes (4096x14336 and 70B gate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
     ap.add_argument("--mode", choices=sorted(ENTRY), default="accumulate",
@@ -311,15 +336,16 @@ def main():
             del p
 
     sweep = {}
-    if args.sweep:
+    names = (SWEEP if args.sweep else []) + (SWEEP_BMAX if args.sweep_bmax else [])
+    if names:
         layers = {}
-        for name in SWEEP:
-            K, N, cfg, mat, _, _ = WORKLOADS[name]
-            key = (K, N, cfg, mat)
+        for name in names:
+            K, N, cfg, mat, _, lv = WORKLOADS[name]
+            key = (K, N, cfg, mat, bmax_of(lv))
             if key not in layers:
                 layers.clear()
                 torch.cuda.empty_cache()
-                layers[key] = Layer(K, N, cfg, mat)
+                layers[key] = Layer(K, N, cfg, mat, bmax_of(lv))
             p = Prepared(name, args.mode, layer=layers[key])
             m, b = p.run(min(args.steps, 100), args.warmup)
             sweep[name] = {"us_per_vmm": m * 1e3, "GB_s": b / (m * 1e-3) / 1e9,
@@ -328,7 +354,7 @@ def main():
             log(f"{name}: {m * 1e3:.2f} us/VMM, {sweep[name]['GB_s']:.1f} GB/s, avg bits {sweep[name]['avg_bits']:.2f}")
             del p
         layers.clear()
-        fit_pts = [(v["bytes"], v["us_per_vmm"]) for k, v in sweep.items() if k.startswith("llama3-70b-gate")]
+        fit_pts = [(v["bytes"], v["us_per_vmm"]) for k, v in sweep.items() if k.startswith("llama3-70b-gate-8192x28672-avg")]
         if len(fit_pts) >= 3:
             sweep["linear_fit_70b_gate"] = linear_fit(fit_pts)
             log(f"70B gate linear fit: {sweep['linear_fit_70b_gate']}")
@@ -348,11 +374,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded N(0,0.02) weights, RTN 8-bit codes, log-normal |x| with 1% outlier channels)",
+        "data": f"synthetic (seeded N(0,0.02) weights, RTN {prep.b_max}-bit codes, log-normal |x| "
+                "with 1% outlier channels)",
         "config": {"workload": args.workload, "entry_point": ENTRY[args.mode], "K": prep.K, "N": prep.N,
+                   "b_max": prep.b_max,
                    "avg_bits": float(np.mean(prep.avg_bits)), "bytes_per_step": step_bytes,
                    "rotated_copies": prep.R, "graph_replay": not args.no_graph,
-                   "arithmetic": "fp16 x times 8-bit codes (as fp16 subnormals) into fp32 accumulators, fp32 dequant",
+                   "arithmetic": "fp16 x times codes (as fp16 subnormals) into fp32 accumulators, fp32 dequant",
                    "thresholds": prep.thresholds, "levels": list(prep.levels)},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},

@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(HERE, "libgrinqh.so")
 GROUP = 128
 TILE = 1024
 MAX_THRESHOLDS = 8
+MAX_BITS = 8
 
 OK, EINVAL, EDEVICE = 0, -1, -2
 
@@ -46,15 +47,16 @@ _SIGNATURES = {
     "grinqh_layout_version": ([], _i32),
     "grinqh_status_string": ([_i32], ctypes.c_char_p),
     "grinqh_last_error": ([], ctypes.c_char_p),
-    "grinqh_planes_bytes": ([_i64, _i64], _i64),
+    "grinqh_planes_bytes": ([_i64, _i64, _i32], _i64),
     "grinqh_workspace_bytes": ([_i64, _i64], _i64),
     "grinqh_workspace_init": ([_vp, _sz, _vp], _i32),
-    "grinqh_pack": ([_vp, _i64, _i64, _vp, _vp], _i32),
+    "grinqh_pack": ([_vp, _i64, _i64, _i32, _vp, _vp], _i32),
     "grinqh_calibrate": ([_vp, _i64, _i64, _vp, _i32, _vp, _vp], _i32),
     "grinqh_assign_bits": ([_vp, _i64, _vp, _vp, _i32, _vp, _vp, _vp, _vp], _i32),
-    "grinqh_vmm": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp], _i32),
-    "grinqh_decode_vmm": ([_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
-    "grinqh_decode_vmm_accumulate": ([_vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
+    "grinqh_vmm": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
+    "grinqh_decode_vmm": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
+    "grinqh_decode_vmm_accumulate": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp],
+                                     _i32),
 }
 
 
@@ -103,8 +105,11 @@ def layout_version() -> int:
     return lib().grinqh_layout_version()
 
 
-def planes_bytes(K: int, N: int) -> int:
-    return lib().grinqh_planes_bytes(K, N)
+def planes_bytes(K: int, N: int, b_max: int = MAX_BITS) -> int:
+    n = lib().grinqh_planes_bytes(K, N, b_max)
+    if n < 0:
+        raise ValueError(f"no store for K = {K}, N = {N}, b_max = {b_max}")
+    return n
 
 
 def workspace_bytes(K: int, N: int) -> int:
@@ -124,15 +129,16 @@ def make_workspace(K: int, N: int, device="cuda", stream=None):
     return ws
 
 
-def pack(codes, out=None, stream=None):
-    """8-bit codes u8 [K][N] (device) -> bit-plane store u8 [planes_bytes(K, N)]."""
+def pack(codes, out=None, stream=None, b_max: int = MAX_BITS):
+    """b_max-bit codes u8 [K][N] (device) -> bit-plane store u8 [planes_bytes(K, N, b_max)]."""
     import torch
-    K, N = codes.shape
     _dev(codes, "codes", torch.uint8)
+    K, N = codes.shape
+    nbytes = planes_bytes(K, N, b_max)
     if out is None:
-        out = torch.empty(planes_bytes(K, N), dtype=torch.uint8, device=codes.device)
-    _dev(out, "planes", torch.uint8, (planes_bytes(K, N),))
-    _check("grinqh_pack", lib().grinqh_pack(codes.data_ptr(), K, N, out.data_ptr(), _stream(stream)))
+        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _dev(out, "planes", torch.uint8, (nbytes,))
+    _check("grinqh_pack", lib().grinqh_pack(codes.data_ptr(), K, N, b_max, out.data_ptr(), _stream(stream)))
     return out
 
 
@@ -181,19 +187,19 @@ def assign_bits(x, thresholds: Sequence[float], levels: Sequence[int], bits=None
     return bits, active_idx, n_active
 
 
-def _check_layer(planes, scales, zeros, x, K, N):
+def _check_layer(planes, scales, zeros, x, K, N, b_max):
     import torch
-    _dev(planes, "planes", torch.uint8, (planes_bytes(K, N),))
+    _dev(planes, "planes", torch.uint8, (planes_bytes(K, N, b_max),))
     _dev(scales, "scales", torch.float16, (n_groups(K), N))
     _dev(zeros, "zeros", torch.float16, (n_groups(K), N))
     _dev(x, "x", torch.float16, (K,))
 
 
 def vmm(planes, scales, zeros, x, bits, active_idx, n_active, K: int, N: int, workspace,
-        out=None, stream=None):
+        out=None, stream=None, b_max: int = MAX_BITS):
     """y fp32 [N] from an explicit assignment (bits, active list, its length)."""
     import torch
-    _check_layer(planes, scales, zeros, x, K, N)
+    _check_layer(planes, scales, zeros, x, K, N, b_max)
     _dev(bits, "bits", torch.uint8, (K,))
     _dev(active_idx, "active_idx", torch.int32)
     _dev(n_active, "n_active", torch.int32, (1,))
@@ -202,38 +208,38 @@ def vmm(planes, scales, zeros, x, bits, active_idx, n_active, K: int, N: int, wo
     _dev(out, "y", torch.float32, (N,))
     _check("grinqh_vmm", lib().grinqh_vmm(
         planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), x.data_ptr(), bits.data_ptr(),
-        active_idx.data_ptr(), n_active.data_ptr(), K, N, out.data_ptr(),
+        active_idx.data_ptr(), n_active.data_ptr(), K, N, b_max, out.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out
 
 
 def decode_vmm(planes, scales, zeros, x, K: int, N: int, thresholds: Sequence[float],
-               levels: Sequence[int], workspace, out=None, stream=None):
+               levels: Sequence[int], workspace, out=None, stream=None, b_max: int = MAX_BITS):
     """The fused decode step: assignment and VMM in one launch; returns y fp32 [N]."""
     import torch
-    _check_layer(planes, scales, zeros, x, K, N)
+    _check_layer(planes, scales, zeros, x, K, N, b_max)
     _dev(workspace, "workspace", torch.uint8)
     out = torch.empty(N, dtype=torch.float32, device=x.device) if out is None else out
     _dev(out, "y", torch.float32, (N,))
     th, lv, n = _host_thresholds(thresholds, levels)
     _check("grinqh_decode_vmm", lib().grinqh_decode_vmm(
-        planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), x.data_ptr(), K, N,
+        planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), x.data_ptr(), K, N, b_max,
         ctypes.cast(th, _vp), ctypes.cast(lv, _vp), n, out.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out
 
 
 def decode_vmm_accumulate(planes, scales, zeros, x, K: int, N: int, thresholds: Sequence[float],
-                          levels: Sequence[int], y, clear=None, stream=None):
+                          levels: Sequence[int], y, clear=None, stream=None, b_max: int = MAX_BITS):
     """y += the fused decode step's product (fp32 atomics, no workspace); zeroes `clear` if given."""
     import torch
-    _check_layer(planes, scales, zeros, x, K, N)
+    _check_layer(planes, scales, zeros, x, K, N, b_max)
     _dev(y, "y", torch.float32, (N,))
     if clear is not None:
         _dev(clear, "clear", torch.float32, (N,))
     th, lv, n = _host_thresholds(thresholds, levels)
     _check("grinqh_decode_vmm_accumulate", lib().grinqh_decode_vmm_accumulate(
-        planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), x.data_ptr(), K, N,
+        planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), x.data_ptr(), K, N, b_max,
         ctypes.cast(th, _vp), ctypes.cast(lv, _vp), n, y.data_ptr(),
         clear.data_ptr() if clear is not None else None, _stream(stream)))
     return y

@@ -26,7 +26,9 @@ int check_launch(const char* what) {
 
 static inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-static int check_assign_params(const float* thresholds, const uint8_t* levels, int n, AssignParams* ap) {
+// max_level: the widest level allowed (8, or the store's b_max for the fused VMM).
+static int check_assign_params(const float* thresholds, const uint8_t* levels, int n, int max_level,
+                               AssignParams* ap) {
   if (n < 0 || n > kMaxThresholds) return fail(GRINQH_EINVAL, "n = %d thresholds, expected 0..%d", n, kMaxThresholds);
   if (n > 0 && !thresholds) return fail(GRINQH_EINVAL, "thresholds is NULL");
   if (!levels) return fail(GRINQH_EINVAL, "levels is NULL");
@@ -39,7 +41,8 @@ static int check_assign_params(const float* thresholds, const uint8_t* levels, i
     ap->th[t] = v;
   }
   for (int t = 0; t <= n; ++t) {
-    if (levels[t] > GRINQH_MAX_BITS) return fail(GRINQH_EINVAL, "level %d is %u (must be 0..8)", t, (unsigned)levels[t]);
+    if (levels[t] > max_level)
+      return fail(GRINQH_EINVAL, "level %d is %u (must be 0..%d)", t, (unsigned)levels[t], max_level);
     ap->lv[t] = levels[t];
   }
   // Unused slots: thresholds +inf and levels[n] repeated, so the kernels
@@ -52,18 +55,23 @@ static int check_assign_params(const float* thresholds, const uint8_t* levels, i
   return GRINQH_OK;
 }
 
-static int check_layer(const void* planes, const void* scales, const void* zeros, const void* x,
-                       const void* y, int64_t K, int64_t N) {
-  if (!planes || !scales || !zeros || !x || !y) return fail(GRINQH_EINVAL, "NULL data pointer");
+static int check_shape(int64_t K, int64_t N, int b_max) {
   if (K <= 0 || N <= 0) return fail(GRINQH_EINVAL, "K = %lld, N = %lld must be positive", (long long)K, (long long)N);
   if (K >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "K or N too large");
+  if (b_max < 1 || b_max > GRINQH_MAX_BITS) return fail(GRINQH_EINVAL, "b_max = %d, expected 1..8", b_max);
   if (K * padded_cols(N) >= (int64_t(1) << 40)) return fail(GRINQH_EINVAL, "store larger than 2^40 bytes");
   return GRINQH_OK;
 }
 
+static int check_layer(const void* planes, const void* scales, const void* zeros, const void* x,
+                       const void* y, int64_t K, int64_t N, int b_max) {
+  if (!planes || !scales || !zeros || !x || !y) return fail(GRINQH_EINVAL, "NULL data pointer");
+  return check_shape(K, N, b_max);
+}
+
 static int check_vmm_common(const void* planes, const void* scales, const void* zeros, const void* x,
-                            const void* y, int64_t K, int64_t N, const void* ws, size_t ws_bytes) {
-  const int st = check_layer(planes, scales, zeros, x, y, K, N);
+                            const void* y, int64_t K, int64_t N, int b_max, const void* ws, size_t ws_bytes) {
+  const int st = check_layer(planes, scales, zeros, x, y, K, N, b_max);
   if (st != GRINQH_OK) return st;
   const VmmGeometry g = vmm_geometry(K, N);
   if (!ws && g.bytes > 0) return fail(GRINQH_EINVAL, "workspace is NULL");
@@ -78,7 +86,7 @@ using namespace grinqh;
 
 extern "C" {
 
-int grinqh_layout_version(void) { return 3; }
+int grinqh_layout_version(void) { return 4; }
 
 const char* grinqh_status_string(int status) {
   switch (status) {
@@ -91,9 +99,9 @@ const char* grinqh_status_string(int status) {
 
 const char* grinqh_last_error(void) { return g_last_error; }
 
-int64_t grinqh_planes_bytes(int64_t K, int64_t N) {
-  if (K <= 0 || N <= 0) return -1;
-  return K * padded_cols(N);
+int64_t grinqh_planes_bytes(int64_t K, int64_t N, int b_max) {
+  if (K <= 0 || N <= 0 || b_max < 1 || b_max > GRINQH_MAX_BITS) return -1;
+  return K * padded_cols(N) / 8 * b_max;
 }
 
 int64_t grinqh_workspace_bytes(int64_t K, int64_t N) {
@@ -108,13 +116,12 @@ int grinqh_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
   return launch_fill_zero(workspace, workspace_bytes, as_stream(stream));
 }
 
-int grinqh_pack(const uint8_t* codes, int64_t K, int64_t N, uint8_t* planes, void* stream) {
+int grinqh_pack(const uint8_t* codes, int64_t K, int64_t N, int b_max, uint8_t* planes, void* stream) {
   g_last_error[0] = 0;
   if (!codes || !planes) return fail(GRINQH_EINVAL, "NULL pointer");
-  if (K <= 0 || N <= 0) return fail(GRINQH_EINVAL, "K = %lld, N = %lld must be positive", (long long)K, (long long)N);
-  if (K >= (int64_t(1) << 31) || N >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "K or N too large");
-  if (K * padded_cols(N) >= (int64_t(1) << 40)) return fail(GRINQH_EINVAL, "store larger than 2^40 bytes");
-  return launch_pack(codes, K, N, planes, as_stream(stream));
+  const int st = check_shape(K, N, b_max);
+  if (st != GRINQH_OK) return st;
+  return launch_pack(codes, K, N, b_max, planes, as_stream(stream));
 }
 
 int grinqh_calibrate(const uint16_t* calib, int64_t V, int64_t K, const double* P, int n_levels,
@@ -144,42 +151,42 @@ int grinqh_assign_bits(const uint16_t* x, int64_t K, const float* thresholds, co
   if (!x || !bits || !active_idx || !n_active) return fail(GRINQH_EINVAL, "NULL pointer");
   if (K <= 0 || K >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "K = %lld out of range", (long long)K);
   AssignParams ap;
-  int st = check_assign_params(thresholds, levels, n, &ap);
+  int st = check_assign_params(thresholds, levels, n, GRINQH_MAX_BITS, &ap);
   if (st != GRINQH_OK) return st;
   return launch_assign(x, K, ap, bits, active_idx, n_active, as_stream(stream));
 }
 
 int grinqh_vmm(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                const uint16_t* x, const uint8_t* bits, const int32_t* active_idx,
-               const int32_t* n_active, int64_t K, int64_t N, float* y,
+               const int32_t* n_active, int64_t K, int64_t N, int b_max, float* y,
                void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
-  int st = check_vmm_common(planes, scales, zeros, x, y, K, N, workspace, workspace_bytes);
+  int st = check_vmm_common(planes, scales, zeros, x, y, K, N, b_max, workspace, workspace_bytes);
   if (st != GRINQH_OK) return st;
   if (!bits || !active_idx || !n_active) return fail(GRINQH_EINVAL, "NULL assignment pointer");
-  return launch_vmm_list(planes, scales, zeros, x, bits, active_idx, n_active, K, N, y, workspace,
+  return launch_vmm_list(planes, scales, zeros, x, bits, active_idx, n_active, K, N, b_max, y, workspace,
                          as_stream(stream));
 }
 
 int grinqh_decode_vmm(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
-                      const uint16_t* x, int64_t K, int64_t N,
+                      const uint16_t* x, int64_t K, int64_t N, int b_max,
                       const float* thresholds, const uint8_t* levels, int n, float* y,
                       void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
-  int st = check_vmm_common(planes, scales, zeros, x, y, K, N, workspace, workspace_bytes);
+  int st = check_vmm_common(planes, scales, zeros, x, y, K, N, b_max, workspace, workspace_bytes);
   if (st != GRINQH_OK) return st;
   AssignParams ap;
-  st = check_assign_params(thresholds, levels, n, &ap);
+  st = check_assign_params(thresholds, levels, n, b_max, &ap);
   if (st != GRINQH_OK) return st;
-  return launch_vmm_fused(planes, scales, zeros, x, K, N, ap, y, workspace, as_stream(stream));
+  return launch_vmm_fused(planes, scales, zeros, x, K, N, b_max, ap, y, workspace, as_stream(stream));
 }
 
 int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
-                                 const uint16_t* x, int64_t K, int64_t N,
+                                 const uint16_t* x, int64_t K, int64_t N, int b_max,
                                  const float* thresholds, const uint8_t* levels, int n,
                                  float* y, float* clear, void* stream) {
   g_last_error[0] = 0;
-  int st = check_layer(planes, scales, zeros, x, y, K, N);
+  int st = check_layer(planes, scales, zeros, x, y, K, N, b_max);
   if (st != GRINQH_OK) return st;
   if (clear) {
     const uintptr_t c0 = reinterpret_cast<uintptr_t>(clear), y0 = reinterpret_cast<uintptr_t>(y);
@@ -187,9 +194,9 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
     if (c0 < y0 + len && y0 < c0 + len) return fail(GRINQH_EINVAL, "clear overlaps y");
   }
   AssignParams ap;
-  st = check_assign_params(thresholds, levels, n, &ap);
+  st = check_assign_params(thresholds, levels, n, b_max, &ap);
   if (st != GRINQH_OK) return st;
-  return launch_vmm_accumulate(planes, scales, zeros, x, K, N, ap, y, clear, as_stream(stream));
+  return launch_vmm_accumulate(planes, scales, zeros, x, K, N, b_max, ap, y, clear, as_stream(stream));
 }
 
 }  // extern "C"

@@ -23,6 +23,10 @@ struct AssignParams {
 __host__ __device__ inline int64_t padded_cols(int64_t N) { return (N + 127) / 128 * 128; }
 __host__ __device__ inline int64_t n_tiles(int64_t N) { return (padded_cols(N) + kTile - 1) / kTile; }
 __host__ __device__ inline int64_t n_groups(int64_t K) { return (K + kGroup - 1) / kGroup; }
+// Byte offset in a b_max-bit store of a position that an 8-plane store has at
+// `off8` (row tile starts: every row tile is b_max / 8 as long).  off8 is a
+// multiple of 128 there, so the result is exact.
+__host__ __device__ inline int64_t store_offset(int64_t off8, int bmax) { return off8 / 8 * bmax; }
 
 __device__ inline float half_bits_to_float(uint16_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, h));
@@ -76,21 +80,21 @@ struct VmmGeometry {
 VmmGeometry vmm_geometry(int64_t K, int64_t N);
 
 // Launchers (one per .hip file).
-int launch_pack(const uint8_t* codes, int64_t K, int64_t N, uint8_t* planes, hipStream_t s);
+int launch_pack(const uint8_t* codes, int64_t K, int64_t N, int bmax, uint8_t* planes, hipStream_t s);
 int launch_calibrate(const uint16_t* calib, int64_t V, int64_t K, const double* cuts, int n,
                      float* thresholds, hipStream_t s);
 int launch_assign(const uint16_t* x, int64_t K, const AssignParams& ap, uint8_t* bits,
                   int32_t* active_idx, int32_t* n_active, hipStream_t s);
 int launch_vmm_list(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                     const uint16_t* x, const uint8_t* bits, const int32_t* active_idx,
-                    const int32_t* n_active, int64_t K, int64_t N, float* y, void* ws,
+                    const int32_t* n_active, int64_t K, int64_t N, int bmax, float* y, void* ws,
                     hipStream_t s);
 int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
-                     const uint16_t* x, int64_t K, int64_t N, const AssignParams& ap, float* y,
-                     void* ws, hipStream_t s);
+                     const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
+                     float* y, void* ws, hipStream_t s);
 int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
-                          const uint16_t* x, int64_t K, int64_t N, const AssignParams& ap, float* y,
-                          float* clear, hipStream_t s);
+                          const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
+                          float* y, float* clear, hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 }  // namespace grinqh

@@ -1,13 +1,13 @@
-// Offline packing of 8-bit codes into the MSB-first 1-bit-plane store
+// Offline packing of b_max-bit codes into the MSB-first 1-bit-plane store
 // (GRINQH paper, section 3.3 "Storage Layout and Weight Loading"; Appendix
 // C.1 "Bit-packing" and "Grouping").  Also the workspace fill kernel.
 #include "common.hpp"
 
 namespace grinqh {
 
-// One thread builds the 8 plane words of one (row, 32-column word).
+// One thread builds the b_max plane words of one (row, 32-column word).
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes, int64_t K,
-                                                   int64_t N, uint8_t* __restrict__ planes) {
+                                                   int64_t N, int bmax, uint8_t* __restrict__ planes) {
   const int64_t Np = padded_cols(N);
   const int64_t words_per_row = Np / 32;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -33,21 +33,24 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ c
     }
     d[m] = v;
   }
-  // Plane p word: bit 8j + m = bit (7 - p) of byte j of d[m].
-  uint8_t* base = planes + t * K * kTile + i * ct + 4 * w;
+  // Plane p word: bit 8j + m = bit (b_max - 1 - p) of byte j of d[m].
+  uint8_t* base = planes + store_offset(t * K * kTile + i * ct, bmax) + 4 * w;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    uint32_t word = 0;
+    if (p < bmax) {
+      const int bit = bmax - 1 - p;
+      uint32_t word = 0;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) word |= ((d[m] >> (7 - p)) & 0x01010101u) << m;
-    *reinterpret_cast<uint32_t*>(base + p * (ct / 8)) = word;
+      for (int m = 0; m < 8; ++m) word |= ((d[m] >> bit) & 0x01010101u) << m;
+      *reinterpret_cast<uint32_t*>(base + p * (ct / 8)) = word;
+    }
   }
 }
 
-int launch_pack(const uint8_t* codes, int64_t K, int64_t N, uint8_t* planes, hipStream_t s) {
+int launch_pack(const uint8_t* codes, int64_t K, int64_t N, int bmax, uint8_t* planes, hipStream_t s) {
   const int64_t total = K * (padded_cols(N) / 32);
   const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, K, N, planes);
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, K, N, bmax, planes);
   return check_launch("grinqh_pack");
 }
 

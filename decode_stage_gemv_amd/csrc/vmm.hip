@@ -32,7 +32,9 @@
 //   A_j = sum_i x_i (q_ij with low 8-b_i bits cleared),
 //   H = sum_i x_i phi_i,  X = sum_i x_i,
 // so scale and zero are applied once per column per workgroup, and H and X
-// are plain sums over the group's active rows.
+// are plain sums over the group's active rows.  A store of b_max < 8 bits has
+// b_max planes per row: the network puts plane p at code bit 7 - p as always,
+// so codes come out as q 2^(8 - b_max) and the scale is s 2^(b_max - 8).
 //
 // Output.  Split-K mode writes one partial row per workgroup; the last one to
 // arrive (per-tile counter) adds them in split order, so y does not depend on
@@ -86,6 +88,7 @@ struct VmmArgs {
   unsigned* counters;
   int64_t K, N;
   int splits, tiles, rows;
+  int bmax;   // planes per row of the store (1..8)
   AssignParams ap;
 };
 
@@ -116,9 +119,10 @@ __device__ int64_t wave_lower_bound(const int32_t* __restrict__ idx, int64_t n, 
   return lo;
 }
 
-// phi * x for one row: the midpoint term of section 3.3 (0 at b = 8 and for no row).
-__device__ inline float phi_x(int b, float x) {
-  return (b > 0 && b < 8) ? x * __builtin_bit_cast(float, (uint32_t)(127 + 7 - b) << 23) : 0.0f;
+// phi * x for one row: the midpoint term of section 3.3 in 8-bit code units,
+// 2^(7 - b) (0 at b = b_max, where nothing is truncated, and for no row).
+__device__ inline float phi_x(int b, int bmax, float x) {
+  return (b > 0 && b < bmax) ? x * __builtin_bit_cast(float, (uint32_t)(127 + 7 - b) << 23) : 0.0f;
 }
 
 // acc[4m + j] += x1 * row1 code + x2 * row2 code for the 32 columns of a lane:
@@ -151,16 +155,19 @@ struct RecordRegs {
 // plane 0 (a cache hit; compute_record ignores them), and a padding row or a
 // record the wave does not have uses an out-of-range voffset, which returns
 // 0 and moves no bytes (only the voffset takes part in the range check).
+// lane_off is 4 l for the lanes of a word the tile has (4 l < pb) and
+// kOutOfRange for the others, so that a narrow last tile never reads past
+// its own row tiles: the scalar plane offset is not range-checked.
 template <int kMaxRecords>
 __device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, const uint32_t* src,
-                                   int j, int b, int pb) {
+                                   int j, int b, int pb, uint32_t lane_off) {
   const int h = (threadIdx.x >> 5) & 1;
-  const int ll = threadIdx.x & 31;
   const int jj = j < kMaxRecords ? j : kMaxRecords - 1;   // table index (unused when b = 0)
   const uint32_t s1 = b > 0 ? src[4 * jj + 2 * h] : kOutOfRange;
   const uint32_t s2 = b > 0 ? src[4 * jj + 2 * h + 1] : kOutOfRange;
-  const uint32_t v1 = s1 == kOutOfRange ? kOutOfRange : s1 + 4u * (uint32_t)ll;
-  const uint32_t v2 = s2 == kOutOfRange ? kOutOfRange : s2 + 4u * (uint32_t)ll;
+  // s < 2^17 and kOutOfRange < 2^31, so the sums do not wrap
+  const uint32_t v1 = s1 == kOutOfRange ? kOutOfRange : s1 + lane_off;
+  const uint32_t v2 = s2 == kOutOfRange ? kOutOfRange : s2 + lane_off;
 #pragma unroll
   for (int p = 0; p < 8; ++p)
     r.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)v1, p < b ? p * pb : 0, 0);
@@ -248,6 +255,8 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   const int t0 = tile * kTile;
   const int ct = (Np - t0) < kTile ? (Np - t0) : kTile;   // multiple of 128
   const int pb = ct / 8;                                  // bytes per plane, multiple of 16
+  const int bmax = a.bmax;
+  const int rstride = pb * bmax;                          // bytes per row tile
   uint16_t sc[kCols], zr[kCols];
 #pragma unroll
   for (int u = 0; u < kCols; ++u) {
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
         if (i >= k0 && i < k1) {   // a well-formed list always is
           rq[e] = (int)(i - k0);
           uint32_t bb = a.bits[i];
-          bq[e] = bb > 8u ? 8u : bb;
+          bq[e] = bb > (uint32_t)bmax ? (uint32_t)bmax : bb;
           xq[e] = x[i];
         }
       }
@@ -319,7 +328,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const float xf = bq[e] > 0 ? half_bits_to_float(xq[e]) : 0.0f;
-      hs += phi_x((int)bq[e], xf);
+      hs += phi_x((int)bq[e], bmax, xf);
       xs += xf;
     }
 #pragma unroll
@@ -378,7 +387,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       const int k = cb + (rank >> 2);
       if ((k & (kWaves - 1)) == wid) {
         const int j = k / kWaves;
-        src[4 * j + (rank & 3)] = (uint32_t)rq[e] * (uint32_t)ct;
+        src[4 * j + (rank & 3)] = (uint32_t)rq[e] * (uint32_t)rstride;
         reinterpret_cast<uint16_t*>(cx)[4 * j + (rank & 3)] = xq[e];
       }
     }
@@ -386,7 +395,8 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 
   // buffer descriptor over this group's row tiles of the tile block
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.planes + (int64_t)t0 * a.K + (int64_t)k0 * ct), (short)0, (k1 - k0) * ct, kRsrcWord3);
+      (void*)(a.planes + store_offset((int64_t)t0 * a.K + (int64_t)k0 * ct, bmax)), (short)0,
+      (k1 - k0) * rstride, kRsrcWord3);
 
   float acc[32];
 #pragma unroll
@@ -401,20 +411,21 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     // the compiler's wait counts let j + 1 and j + 2 stay outstanding.
     // Records past nrec load nothing (width 0) and are not computed.
     const int h = (tid >> 5) & 1;
+    const uint32_t lane_off = 4 * (tid & 31) < pb ? 4u * (uint32_t)(tid & 31) : kOutOfRange;
     auto width = [&](int j) { return j < kMaxRecords ? __builtin_amdgcn_readlane(rec_w, j) : 0; };
     RecordRegs rr[3];
     int bw[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       bw[j] = width(j);
-      load_record<kMaxRecords>(rr[j], rsrc, src, j, bw[j], pb);
+      load_record<kMaxRecords>(rr[j], rsrc, src, j, bw[j], pb, lane_off);
     }
 #pragma unroll
     for (int j = 0; j < kMaxRecords; ++j) {
       if (j < nrec) compute_record(rr[j % 3], bw[j % 3], cx[2 * j + h], acc);
       if (j + 3 < kMaxRecords) {
         bw[j % 3] = width(j + 3);
-        load_record<kMaxRecords>(rr[j % 3], rsrc, src, j + 3, bw[j % 3], pb);
+        load_record<kMaxRecords>(rr[j % 3], rsrc, src, j + 3, bw[j % 3], pb, lane_off);
       }
     }
   }
@@ -435,6 +446,9 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   __syncthreads();
   const float H = s_hx[0];
   const float X = s_hx[1];
+  // codes entered as c 2^-24 and stand at q 2^(8 - b_max)
+  const float afac = __builtin_bit_cast(float, (uint32_t)(127 + 24) << 23);
+  const float sfac = __builtin_bit_cast(float, (uint32_t)(127 + bmax - 8) << 23);
   float val[kCols];
 #pragma unroll
   for (int u = 0; u < kCols; ++u) {
@@ -444,8 +458,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       float A = 0.0f;
 #pragma unroll
       for (int h = 0; h < kWaves; ++h) A += red[(h * 32 + (col >> 5)) * kRedStride + (col & 31)];
-      A *= 16777216.0f;   // codes entered as c * 2^-24
-      val[u] = half_bits_to_float(sc[u]) * (A + H) + half_bits_to_float(zr[u]) * X;
+      val[u] = (half_bits_to_float(sc[u]) * sfac) * (A * afac + H) + half_bits_to_float(zr[u]) * X;
     }
   }
 
@@ -572,30 +585,30 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_
 
 int launch_vmm_list(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                     const uint16_t* x, const uint8_t* bits, const int32_t* active_idx,
-                    const int32_t* n_active, int64_t K, int64_t N, float* y, void* ws,
+                    const int32_t* n_active, int64_t K, int64_t N, int bmax, float* y, void* ws,
                     hipStream_t s) {
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.bits = bits; a.active_idx = active_idx; a.n_active = n_active;
-  a.y = y; a.K = K; a.N = N;
+  a.y = y; a.K = K; a.N = N; a.bmax = bmax;
   return launch_vmm(false, kOutSplitK, a, ws, s);
 }
 
 int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
-                     const uint16_t* x, int64_t K, int64_t N, const AssignParams& ap, float* y,
-                     void* ws, hipStream_t s) {
+                     const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
+                     float* y, void* ws, hipStream_t s) {
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
-  a.y = y; a.K = K; a.N = N; a.ap = ap;
+  a.y = y; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
   return launch_vmm(true, kOutSplitK, a, ws, s);
 }
 
 int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
-                          const uint16_t* x, int64_t K, int64_t N, const AssignParams& ap, float* y,
-                          float* clear, hipStream_t s) {
+                          const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
+                          float* y, float* clear, hipStream_t s) {
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
-  a.y = y; a.clear = clear; a.K = K; a.N = N; a.ap = ap;
+  a.y = y; a.clear = clear; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
   return launch_vmm(true, kOutAccumulate, a, nullptr, s);
 }
 

@@ -4,12 +4,14 @@
  *
  * Method: "GRINQH: Graded Input-based Quantization Hierarchy for Efficient
  * LLM Generation" (arXiv 2606.23419).  At batch size 1, y = x W over one
- * linear layer, W stored input-major (row i = input channel i).  Each row i
- * gets a bit width b_i in {0..8} from |x_i| and calibrated thresholds
- * (section 3.1); only the b_i most significant bit planes of that row are
- * read from a nested bit-plane store (section 3.3, Appendix C.1); the
- * truncated code is rebuilt with the midpoint term and dequantised with the
- * row group's scale and zero (section 3.3), and products accumulate in fp32.
+ * linear layer, W stored input-major (row i = input channel i) as b_max-bit
+ * codes (b_max = 8, or a smaller maximum width such as the 4 and 6 of
+ * section 3.3).  Each row i gets a bit width b_i in {0..b_max} from |x_i| and
+ * calibrated thresholds (section 3.1); only the b_i most significant bit
+ * planes of that row are read from a nested bit-plane store (section 3.3,
+ * Appendix C.1); the truncated code is rebuilt with the midpoint term and
+ * dequantised with the row group's scale and zero (section 3.3), and products
+ * accumulate in fp32.
  *
  * Conventions shared by every call below
  * - Pointers are DEVICE pointers unless the argument says "host".  The caller
@@ -25,13 +27,16 @@
  *   on one stream, or give each stream its own workspace).
  *
  * Store layout (this library's concrete form of the paper's bit-planar
- * store; grinqh_layout_version() == 3):
+ * store; grinqh_layout_version() == 4), for b_max-bit codes, 1 <= b_max <= 8:
  * - N_pad = N rounded up to a multiple of 128.  Columns are cut into tiles of
  *   GRINQH_TILE = 1024 columns; tile t has width C_t = min(1024, N_pad - 1024 t).
- * - Tile t occupies bytes [1024 K t, 1024 K t + K C_t).  Inside it, row tile
- *   (t, i) starts at 1024 K t + i C_t and holds planes 0..7 back to back,
- *   C_t / 8 bytes each; plane p holds bit (7 - p) of the 8-bit code, so the
- *   top b planes of a row are one contiguous span of b C_t / 8 bytes.
+ * - Let R = b_max / 8.  Tile t occupies bytes [1024 K t R, (1024 K t + K C_t) R).
+ *   Inside it, row tile (t, i) starts at (1024 K t + i C_t) R and holds planes
+ *   0 .. b_max - 1 back to back, C_t / 8 bytes each; plane p holds bit
+ *   (b_max - 1 - p) of the code, so the top b planes of a row are one
+ *   contiguous span of b C_t / 8 bytes.  At b_max = 8 this is the full 8-plane
+ *   store; a smaller b_max keeps only the planes it has (section 3.3 and
+ *   Appendix C.1: the format does not depend on the maximum width).
  * - A plane is a run of little-endian 32-bit words, one per 32 columns.  In
  *   the word for columns 32w .. 32w + 31 of the tile, column 32w + 4m + j
  *   (m = 0..7, j = 0..3) sits at bit 8j + m.
@@ -59,9 +64,9 @@ enum {
 #define GRINQH_GROUP 128          /* rows per (scale, zero) group */
 #define GRINQH_TILE 1024          /* columns per row tile of the store */
 #define GRINQH_MAX_THRESHOLDS 8   /* n <= 8 thresholds, n + 1 <= 9 levels */
-#define GRINQH_MAX_BITS 8         /* b_max */
+#define GRINQH_MAX_BITS 8         /* largest b_max */
 
-/* Version of the store layout described above (3). */
+/* Version of the store layout described above (4). */
 int grinqh_layout_version(void);
 
 /* Static description of a status code.  Never NULL. */
@@ -70,9 +75,10 @@ const char* grinqh_status_string(int status);
 /* Message for the most recent failed call on this host thread ("" if none). */
 const char* grinqh_last_error(void);
 
-/* Size in bytes of the bit-plane store for K rows and N columns: K * N_pad.
- * Returns -1 if K <= 0 or N <= 0. */
-int64_t grinqh_planes_bytes(int64_t K, int64_t N);
+/* Size in bytes of the bit-plane store for K rows and N columns of b_max-bit
+ * codes: K * N_pad * b_max / 8.  Returns -1 if K <= 0, N <= 0 or b_max is
+ * outside 1..8. */
+int64_t grinqh_planes_bytes(int64_t K, int64_t N, int b_max);
 
 /* Workspace bytes grinqh_vmm / grinqh_decode_vmm need for a K x N layer
  * (split-K partial sums and per-tile counters).  Returns -1 for K, N <= 0. */
@@ -87,11 +93,14 @@ int grinqh_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
 /*
  * Offline packing (section 3.3 "Storage Layout and Weight Loading";
  * Appendix C.1 "Bit-packing", "Grouping").
- * codes:  u8 [K][N] row-major, the b_max = 8 bit codes (row = input channel).
- * planes: u8 [grinqh_planes_bytes(K, N)], written completely (padding too).
- * Errors: EINVAL for NULL pointers or K, N <= 0 or K * N_pad >= 2^40.
+ * codes:  u8 [K][N] row-major, b_max-bit codes (row = input channel), each
+ *         below 2^b_max; only the low b_max bits of a code are stored.
+ * b_max:  1..8, the planes per row of the store.
+ * planes: u8 [grinqh_planes_bytes(K, N, b_max)], written completely (padding too).
+ * Errors: EINVAL for NULL pointers, K, N <= 0, b_max outside 1..8 or
+ * K * N_pad >= 2^40.
  */
-int grinqh_pack(const uint8_t* codes, int64_t K, int64_t N, uint8_t* planes, void* stream);
+int grinqh_pack(const uint8_t* codes, int64_t K, int64_t N, int b_max, uint8_t* planes, void* stream);
 
 /*
  * Offline threshold calibration by percentile mapping (section 3.2;
@@ -129,35 +138,39 @@ int grinqh_assign_bits(const uint16_t* x, int64_t K, const float* thresholds, co
 /*
  * The decode-stage VMM from an explicit assignment (section 3.3).
  * y[j] = sum over listed rows i of x_i (s[g][j] r_ij + z[g][j]), g = i / 128,
- * r_ij = (q_ij with its low 8 - b_i bits cleared) + phi_i, phi_i = 2^(7 - b_i)
- * for b_i < 8 and 0 for b_i = 8; only the top b_i planes of a row are read.
- * planes:     the store (layout above) for K x N.
- * scales, zeros: fp16 [ceil(K/128)][N].
+ * r_ij = (q_ij with its low b_max - b_i bits cleared) + phi_i,
+ * phi_i = 2^(b_max - 1 - b_i) for b_i < b_max and 0 for b_i = b_max; only
+ * the top b_i planes of a row are read.
+ * planes:     the store (layout above) for K x N, packed with this b_max.
+ * scales, zeros: fp16 [ceil(K/128)][N], the step and offset of the b_max-bit
+ *             codes (w = s q + z).
  * x:          fp16 [K].
- * bits:       u8 [K]; entries above 8 are treated as 8, rows with 0 add nothing.
+ * bits:       u8 [K]; entries above b_max are treated as b_max, rows with 0
+ *             add nothing.
  * active_idx: i32 [*n_active], strictly ascending, each in [0, K) -- for
  *             example the output of grinqh_assign_bits.
  * n_active:   i32 [1] on the device (read by the kernel; no host sync).
  * y:          fp32 [N] out (written completely).
  * workspace:  grinqh_workspace_bytes(K, N) bytes, zeroed once with
  *             grinqh_workspace_init.
- * Errors: EINVAL for NULL pointers, K, N <= 0, K >= 2^31, or a workspace
- * smaller than grinqh_workspace_bytes(K, N).
+ * Errors: EINVAL for NULL pointers, K, N <= 0, K >= 2^31, b_max outside
+ * 1..8, or a workspace smaller than grinqh_workspace_bytes(K, N).
  */
 int grinqh_vmm(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                const uint16_t* x, const uint8_t* bits, const int32_t* active_idx,
-               const int32_t* n_active, int64_t K, int64_t N, float* y,
+               const int32_t* n_active, int64_t K, int64_t N, int b_max, float* y,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The whole decode step in one launch: assignment (section 3.1) fused into
  * the VMM (section 3.3).  Same result as grinqh_assign_bits followed by
  * grinqh_vmm, without materialising bits or the active list.
- * thresholds/levels/n as in grinqh_assign_bits (host arrays); the remaining
- * arguments as in grinqh_vmm.
+ * thresholds/levels/n as in grinqh_assign_bits (host arrays), with every
+ * level at most b_max (EINVAL otherwise); the remaining arguments as in
+ * grinqh_vmm.
  */
 int grinqh_decode_vmm(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
-                      const uint16_t* x, int64_t K, int64_t N,
+                      const uint16_t* x, int64_t K, int64_t N, int b_max,
                       const float* thresholds, const uint8_t* levels, int n, float* y,
                       void* workspace, size_t workspace_bytes, void* stream);
 
@@ -176,7 +189,7 @@ int grinqh_decode_vmm(const uint8_t* planes, const uint16_t* scales, const uint1
  * Errors: as grinqh_decode_vmm, and EINVAL when clear overlaps y.
  */
 int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
-                                 const uint16_t* x, int64_t K, int64_t N,
+                                 const uint16_t* x, int64_t K, int64_t N, int b_max,
                                  const float* thresholds, const uint8_t* levels, int n,
                                  float* y, float* clear, void* stream);
 

@@ -34,13 +34,18 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_static_queries(lib):
-    assert lib.grinqh_layout_version() == 3
+    assert lib.grinqh_layout_version() == 4
     assert lib.grinqh_status_string(0) == b"ok"
     assert lib.grinqh_status_string(-1) == b"invalid argument"
     assert lib.grinqh_status_string(-2) == b"device error"
-    assert lib.grinqh_planes_bytes(4096, 14336) == 4096 * 14336
-    assert lib.grinqh_planes_bytes(3, 33) == 3 * 128
-    assert lib.grinqh_planes_bytes(0, 5) == -1
+    assert lib.grinqh_planes_bytes(4096, 14336, 8) == 4096 * 14336
+    assert lib.grinqh_planes_bytes(4096, 14336, 6) == 4096 * 14336 * 6 // 8
+    assert lib.grinqh_planes_bytes(4096, 14336, 4) == 4096 * 14336 // 2
+    assert lib.grinqh_planes_bytes(3, 33, 8) == 3 * 128
+    assert lib.grinqh_planes_bytes(3, 33, 1) == 3 * 16
+    assert lib.grinqh_planes_bytes(0, 5, 8) == -1
+    assert lib.grinqh_planes_bytes(4, 5, 0) == -1
+    assert lib.grinqh_planes_bytes(4, 5, 9) == -1
     assert lib.grinqh_workspace_bytes(-1, 5) == -1
     assert lib.grinqh_workspace_bytes(128, 4096) >= 0
     assert lib.grinqh_workspace_bytes(4096, 14336) >= 4 * 14336
@@ -54,10 +59,12 @@ def _err(lib):
 
 
 def test_pack_validation(lib):
-    assert lib.grinqh_pack(None, 4, 4, FAKE, None) == g.EINVAL
-    assert lib.grinqh_pack(FAKE, 0, 4, FAKE, None) == g.EINVAL
+    assert lib.grinqh_pack(None, 4, 4, 8, FAKE, None) == g.EINVAL
+    assert lib.grinqh_pack(FAKE, 0, 4, 8, FAKE, None) == g.EINVAL
     assert "positive" in _err(lib)
-    assert lib.grinqh_pack(FAKE, 4, -3, FAKE, None) == g.EINVAL
+    assert lib.grinqh_pack(FAKE, 4, -3, 8, FAKE, None) == g.EINVAL
+    assert lib.grinqh_pack(FAKE, 4, 4, 0, FAKE, None) == g.EINVAL and "b_max" in _err(lib)
+    assert lib.grinqh_pack(FAKE, 4, 4, 9, FAKE, None) == g.EINVAL
 
 
 def test_assign_validation(lib):
@@ -83,20 +90,32 @@ def test_assign_validation(lib):
 def test_vmm_validation(lib):
     need = lib.grinqh_workspace_bytes(4096, 4096)
     assert need > 0
-    r = lib.grinqh_vmm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 4096, FAKE, FAKE, need - 1, None)
+    r = lib.grinqh_vmm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 4096, 8, FAKE, FAKE, need - 1, None)
     assert r == g.EINVAL and "workspace" in _err(lib)
-    r = lib.grinqh_vmm(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4096, 4096, FAKE, FAKE, need, None)
+    r = lib.grinqh_vmm(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4096, 4096, 8, FAKE, FAKE, need, None)
     assert r == g.EINVAL
-    r = lib.grinqh_vmm(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 4096, FAKE, FAKE, need, None)
+    r = lib.grinqh_vmm(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 4096, 8, FAKE, FAKE, need, None)
     assert r == g.EINVAL
+    r = lib.grinqh_vmm(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, 4096, 0, FAKE, FAKE, need, None)
+    assert r == g.EINVAL and "b_max" in _err(lib)
     th = (ctypes.c_float * 1)(1.0)
+    thp = ctypes.cast(th, ctypes.c_void_p)
     lv = (ctypes.c_uint8 * 2)(0, 12)
-    r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 4096, 4096, ctypes.cast(th, ctypes.c_void_p),
+    r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 4096, 4096, 8, thp,
                               ctypes.cast(lv, ctypes.c_void_p), 1, FAKE, FAKE, need, None)
     assert r == g.EINVAL
-    r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 0, 4096, ctypes.cast(th, ctypes.c_void_p),
-                              ctypes.cast(lv, ctypes.c_void_p), 1, FAKE, FAKE, need, None)
+    lv8 = (ctypes.c_uint8 * 2)(0, 8)
+    r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 0, 4096, 8, thp,
+                              ctypes.cast(lv8, ctypes.c_void_p), 1, FAKE, FAKE, need, None)
     assert r == g.EINVAL
+    # a level above the store's b_max is rejected
+    lv6 = (ctypes.c_uint8 * 2)(0, 6)
+    r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 4096, 4096, 4, thp,
+                              ctypes.cast(lv6, ctypes.c_void_p), 1, FAKE, FAKE, need, None)
+    assert r == g.EINVAL and "level" in _err(lib)
+    r = lib.grinqh_decode_vmm(FAKE, FAKE, FAKE, FAKE, 4096, 4096, 9, thp,
+                              ctypes.cast(lv8, ctypes.c_void_p), 1, FAKE, FAKE, need, None)
+    assert r == g.EINVAL and "b_max" in _err(lib)
 
 
 def test_accumulate_validation(lib):
@@ -105,12 +124,14 @@ def test_accumulate_validation(lib):
     thp, lvp = ctypes.cast(th, ctypes.c_void_p), ctypes.cast(lv, ctypes.c_void_p)
     y = 0x100000
     # clear overlapping y is rejected; clear == NULL is allowed (fails later only on bad args)
-    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, thp, lvp, 1, y, y + 128, None)
+    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, 1, y, y + 128, None)
     assert r == g.EINVAL and "overlap" in _err(lib)
-    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, thp, lvp, 1, None, None, None)
+    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, 1, None, None, None)
     assert r == g.EINVAL
-    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, thp, lvp, -2, y, None, None)
+    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, -2, y, None, None)
     assert r == g.EINVAL
+    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, 6, thp, lvp, 1, y, None, None)
+    assert r == g.EINVAL and "level" in _err(lib)
 
 
 def test_calibrate_validation(lib):
