@@ -324,6 +324,37 @@ def decode_step(codes, scales, zeros, x, thresholds, levels, b_max: int = B_MAX)
 
 
 # --------------------------------------------------------------------------
+# Dense prefill -- section 3 (the prefill stage loads weights at a fixed
+# precision), section 4 "Prefill vs. Decoding Evaluation" (the kernel unpacks
+# the weights at full b_max precision and multiplies densely) and section 5
+# "End-to-end Measurements".
+# --------------------------------------------------------------------------
+
+def dequant_dense(codes, scales, zeros, b_max: int = B_MAX) -> np.ndarray:
+    """W_hat = s q + z for every row at its full width b_max, fp64 [K][N].
+
+    At b = b_max nothing is truncated and phi = 0 (the reading of section 3.3
+    used throughout), so the dense weights are the parent model's.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    K = codes.shape[0]
+    rows = np.arange(K)
+    return _dequant_rows(codes, scales, zeros, rows, np.full(K, _check_bmax(b_max)), b_max)
+
+
+def prefill(codes, scales, zeros, X, b_max: int = B_MAX) -> np.ndarray:
+    """Y = X W_hat in fp64 for a batch of M token activations X fp16 [M][K]."""
+    X64 = np.asarray(X, dtype=np.float16).astype(np.float64)
+    return X64 @ dequant_dense(codes, scales, zeros, b_max)
+
+
+def prefill_abs(codes, scales, zeros, X, b_max: int = B_MAX) -> np.ndarray:
+    """|X| |W_hat| (the tolerance scale of the prefill product)."""
+    X64 = np.abs(np.asarray(X, dtype=np.float16).astype(np.float64))
+    return X64 @ np.abs(dequant_dense(codes, scales, zeros, b_max))
+
+
+# --------------------------------------------------------------------------
 # Bytes accounting.
 # --------------------------------------------------------------------------
 
