@@ -9,7 +9,7 @@ call raises.
 
 Names follow the C ABI in ``include/grinqh.h``:
 ``pack``, ``calibrate``, ``assign_bits``, ``vmm``, ``decode_vmm``,
-``decode_vmm_accumulate``.
+``decode_vmm_accumulate``, ``prefill``.
 """
 from __future__ import annotations
 
@@ -57,6 +57,7 @@ _SIGNATURES = {
     "grinqh_decode_vmm": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
     "grinqh_decode_vmm_accumulate": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp],
                                      _i32),
+    "grinqh_prefill": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
 }
 
 
@@ -243,3 +244,19 @@ def decode_vmm_accumulate(planes, scales, zeros, x, K: int, N: int, thresholds: 
         ctypes.cast(th, _vp), ctypes.cast(lv, _vp), n, y.data_ptr(),
         clear.data_ptr() if clear is not None else None, _stream(stream)))
     return y
+
+
+def prefill(planes, scales, zeros, X, K: int, N: int, out=None, stream=None, b_max: int = MAX_BITS):
+    """Dense prefill of a token batch: Y fp32 [M][N] = X fp16 [M][K] times the full-width weights."""
+    import torch
+    _dev(X, "X", torch.float16)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError(f"X must be [M][{K}], got {tuple(X.shape)}")
+    M = X.shape[0]
+    _check_layer(planes, scales, zeros, X[0], K, N, b_max)
+    out = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _dev(out, "Y", torch.float32, (M, N))
+    _check("grinqh_prefill", lib().grinqh_prefill(
+        planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), X.data_ptr(), M, K, N, b_max,
+        out.data_ptr(), _stream(stream)))
+    return out

@@ -199,4 +199,13 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
   return launch_vmm_accumulate(planes, scales, zeros, x, K, N, b_max, ap, y, clear, as_stream(stream));
 }
 
+int grinqh_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                   const uint16_t* X, int64_t M, int64_t K, int64_t N, int b_max, float* Y, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_layer(planes, scales, zeros, X, Y, K, N, b_max);
+  if (st != GRINQH_OK) return st;
+  if (M <= 0 || M >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "M = %lld out of range", (long long)M);
+  return launch_prefill(planes, scales, zeros, X, M, K, N, b_max, Y, as_stream(stream));
+}
+
 }  // extern "C"

@@ -193,6 +193,25 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
                                  const float* thresholds, const uint8_t* levels, int n,
                                  float* y, float* clear, void* stream);
 
+/*
+ * Dense prefill of a batch of M tokens (section 3: the prefill stage loads
+ * weights at one fixed precision; section 4 "Prefill vs. Decoding
+ * Evaluation": weights are unpacked at full b_max precision and multiplied
+ * densely).  Every row is read at its full width b_max (nothing truncated, no
+ * midpoint term):
+ *   Y[m][n] = sum_k X[m][k] w[k][n],  w[k][n] = s[k/128][n] q[k][n] + z[k/128][n],
+ * with w rounded to fp16 once (a fused multiply-add) and products summed in
+ * fp32 on the matrix cores.
+ * planes:        the store (layout above) for K x N, packed with this b_max.
+ * scales, zeros: fp16 [ceil(K/128)][N].
+ * X:             fp16 [M][K] row-major (token m's activations in row m).
+ * Y:             fp32 [M][N] row-major out (written completely).
+ * Errors: EINVAL for NULL pointers, M, K, N <= 0, M or K or N >= 2^31,
+ * b_max outside 1..8, or M above 65535 * 128.
+ */
+int grinqh_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                   const uint16_t* X, int64_t M, int64_t K, int64_t N, int b_max, float* Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

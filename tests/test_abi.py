@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for name in names:
         assert hasattr(lib, name), name
         assert name in g._SIGNATURES, name
@@ -156,3 +156,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(g, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         g.lib()
+
+
+def test_prefill_validation(lib):
+    assert lib.grinqh_prefill(None, FAKE, FAKE, FAKE, 4, 128, 64, 8, FAKE, None) == g.EINVAL
+    assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 0, 128, 64, 8, FAKE, None) == g.EINVAL
+    assert "M" in _err(lib)
+    assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 4, 0, 64, 8, FAKE, None) == g.EINVAL
+    assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 4, 128, 64, 9, FAKE, None) == g.EINVAL
+    assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 65535 * 128 + 1, 128, 64, 8, FAKE, None) == g.EINVAL
