@@ -232,6 +232,76 @@ class Prepared:
         return ms, step_bytes
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
+
+
+def _graph_time(fn, steps, warmup):
+    """Microseconds per call of fn over one HIP-graph replay of `steps` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(steps):
+                fn()
+        g.replay()
+        s.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(s)
+        g.replay()
+        stop.record(s)
+        s.synchronize()
+    return start.elapsed_time(stop) * 1e3 / steps
+
+
+def prefill_bench(layer, M, steps=20, warmup=3, dense_reference=True):
+    """Dense prefill of M tokens through grinqh_prefill (every row at b_max).
+
+    Reports TFLOP/s over 2 M K N flops against the dense fp16 matrix-core peak.
+    For context it also times torch.matmul on the same weights dequantised to
+    a dense fp16 matrix (a plain library GEMM that reads 2 bytes per weight;
+    not part of this library's path)."""
+    import torch
+    import synthetic
+    import decode_stage_gemv_amd as grq
+    K, N = layer.K, layer.N
+    X = torch.from_numpy(synthetic.make_activations(K, M, config=layer.cfg, matrix=layer.mat)).cuda()
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    state = {"k": 0}
+
+    def step():
+        planes, scales, zeros, _ = layer.copies[state["k"] % layer.R]
+        state["k"] += 1
+        grq.prefill(planes, scales, zeros, X, K, N, out=Y, b_max=layer.b_max)
+
+    us = _graph_time(step, steps, warmup)
+    flops = 2.0 * M * K * N
+    out = {"tokens": M, "K": K, "N": N, "b_max": layer.b_max, "us": us, "TFLOP_s": flops / (us * 1e-6) / 1e12}
+    out["frac_of_mfma_f16_peak"] = out["TFLOP_s"] / MFMA_F16_PEAK_TFLOPS
+    if dense_reference:
+        lay = layer.host
+        g = np.arange(K) // 128
+        W = torch.from_numpy(lay.codes).cuda().to(torch.float32)
+        W.mul_(torch.from_numpy(lay.scales).cuda().to(torch.float32)[g]).add_(
+            torch.from_numpy(lay.zeros).cuda().to(torch.float32)[g])
+        W16 = W.to(torch.float16)
+        del W
+        Yd = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        us_d = _graph_time(lambda: torch.matmul(X, W16, out=Yd), steps, warmup)
+        out["dense_fp16_matmul_us"] = us_d
+        out["dense_fp16_matmul_TFLOP_s"] = flops / (us_d * 1e-6) / 1e12
+        del W16, Yd
+    log(f"prefill {M}x{K}x{N} (b_max {layer.b_max}): {us:.1f} us, {out['TFLOP_s']:.0f} TFLOP/s "
+        f"({out['frac_of_mfma_f16_peak']:.1%} of fp16 MFMA peak)"
+        + (f"; dense fp16 torch.matmul {out['dense_fp16_matmul_us']:.1f} us" if dense_reference else ""))
+    return out
+
+
 def copy_probe(nbytes=512 << 20, reps=20):
     """A plain device-to-device copy of known size: reads nbytes, writes nbytes."""
     import torch
@@ -303,6 +373,10 @@ def main():
     ap.add_argument("--only", action="store_true", help="time only the chosen entry point")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 512 MiB device copy (reference for bandwidth and counters)")
+    ap.add_argument("--prefill-tokens", type=int, default=2048,
+                    help="tokens of the dense prefill timed on the same layer (0: skip)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the dense prefill of the chosen workload's layer")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode VMM path runs on a single GPU "
@@ -315,6 +389,12 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.prefill_only:
+        K, N, cfg, mat, _, lv = WORKLOADS[args.workload]
+        res = prefill_bench(Layer(K, N, cfg, mat, bmax_of(lv)), args.prefill_tokens or 2048,
+                            steps=min(args.steps, 20), warmup=min(args.warmup, 3), dense_reference=False)
+        print(json.dumps({"prefill": res}), flush=True)
         return
     prep = Prepared(args.workload, args.mode)
     ms, step_bytes = prep.run(args.steps, args.warmup, graph=not args.no_graph)
@@ -359,6 +439,10 @@ def main():
             sweep["linear_fit_70b_gate"] = linear_fit(fit_pts)
             log(f"70B gate linear fit: {sweep['linear_fit_70b_gate']}")
 
+    prefill = None
+    if args.prefill_tokens > 0 and not args.only:
+        prefill = prefill_bench(prep.layer, args.prefill_tokens)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(prep)
     traffic = measured_traffic(args.workload, args.mode)
     out = {
@@ -390,6 +474,8 @@ def main():
         out["other_entry_points"] = others
     if sweep:
         out["sweep"] = sweep
+    if prefill:
+        out["prefill"] = prefill
     print(json.dumps(out), flush=True)
 
 

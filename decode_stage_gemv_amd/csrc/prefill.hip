@@ -8,27 +8,37 @@
 //
 // for a batch of M token activations, every row read at its full width.
 //
-// Work split.  A workgroup (4 waves) owns a 128-token x 128-column tile of Y
-// and walks K one scale group (128 rows) at a time; wave (r, c) of the 2 x 2
-// wave grid owns a 64 x 64 quarter as 2 x 2 blocks of 32 x 32, accumulated
-// in fp32 by v_mfma_f32_32x32x16_f16.  The 128 columns lie inside one
-// 1024-column tile of the store.
+// Work split.  A workgroup (8 waves) owns 128 tokens x one 512-column half of
+// a 1024-column store tile (half of every 128-byte plane line it reads; the
+// workgroup of the other half usually runs on the same XCD).  Wave w owns
+// columns 64 w .. 64 w + 63 of the half for all 128 tokens, as 4 x 2 blocks of
+// 32 x 32 accumulated in fp32 by v_mfma_f32_32x32x16_f16, so every weight is
+// dequantised by exactly one wave.  K is walked 64 rows per step.  Unpacking
+// costs vector-ALU work per weight while the matrix work per weight grows
+// with the tokens sharing it, hence the tall tile.
 //
-// Per group:
-//   1. X[m0 .. m0+127][k0 .. k0+127] (fp16) goes to LDS, rows padded by 16
-//      bytes so the A-fragment reads are conflict-free.
-//   2. Each thread rebuilds the codes of two rows x 32 columns from their
-//      b_max plane words (the bit transpose of bitplane.hpp) and writes them
-//      to LDS as exact fp16 integers, the two rows of a pair in one dword:
-//      the B operand of the MFMA wants eight consecutive k of one column per
-//      lane, so the codes are stored column-major in 16-byte fragments of
-//      eight rows, with the column index XOR-swizzled by the fragment row so
-//      that both the writes and the reads are free of bank conflicts.
+// Per step:
+//   1. X[m0 .. m0+127][k0 .. k0+63] (fp16) goes to LDS, rows padded by 16
+//      bytes so that the A-fragment reads are conflict-free.
+//   2. Thread (row pair r, plane word w) rebuilds the codes of its two rows x
+//      32 columns from their b_max plane words (the bit transpose of
+//      bitplane.hpp, specialised for b_max) and writes them to LDS as exact
+//      fp16 integers, the two rows of a pair in one dword.  The B operand of
+//      the MFMA wants eight consecutive k of one column per lane, so codes
+//      are stored column-major in 16-byte fragments of eight rows; inside
+//      each 32-column block the column is XOR-swizzled by the block index,
+//      which makes the writes and the fragment reads conflict-free.
 //   3. Each lane dequantises its B fragments right after reading them:
 //      w = s q + z with one packed fp16 fused multiply-add per two weights
-//      (one rounding to fp16), s and z being constant along a fragment.
-//   4. While the MFMAs of this group run, the loads of the next group's X,
-//      plane words, scales and zeros are already in flight (registers).
+//      (one rounding to fp16); s and z are constant along a fragment.
+//   4. The next step's X, plane words, scales and zeros are loaded into
+//      registers while this step's MFMAs run.  Plane and X loads are buffer
+//      loads: rows past K, tokens past M, words past a narrow tile and
+//      columns past K read as zero through out-of-range offsets, and the
+//      plane index is a scalar offset.
+// Workgroups are numbered so that the ones sharing a column half land on the
+// same XCD (consecutive workgroup ids go to different XCDs), where they read
+// its planes through one L2.
 #include "bitplane.hpp"
 #include "common.hpp"
 
@@ -37,18 +47,32 @@ namespace grinqh {
 namespace {
 
 constexpr int kPM = 128;                // tokens per workgroup tile
-constexpr int kPN = 128;                // columns per workgroup tile
-constexpr int kPK = kGroup;             // rows per step: one scale group
-constexpr int kPThreads = 256;          // 4 waves
+constexpr int kPN = kTile / 2;          // columns per workgroup tile: half a store tile
+constexpr int kPK = 64;                 // rows per step
+constexpr int kPWaves = 8;
+constexpr int kPThreads = 64 * kPWaves;
 constexpr int kXPitch = kPK + 8;        // halves per LDS row of the X tile
-constexpr int kXChunks = kPM * kPK / 8 / kPThreads;   // 16-byte X chunks per thread per step (8)
-constexpr int kFragRows = 8;            // rows per B fragment
-constexpr int kFrags = kPK / kFragRows; // fragment rows per step (16)
+constexpr int kXChunks = kPM * kPK / 8 / kPThreads;   // 16-byte X chunks per thread per step (2)
+constexpr int kFragRows = kPK / 8;      // B fragment rows (of 8 k) per step
+constexpr int kXCDs = 8;                // MI355X
+constexpr uint32_t kOOR = 0x7FFFFF00u;  // buffer offset past every range used here
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+
+// Raw buffer descriptor from values that are the same in every lane; the
+// read-first-lane makes that visible to the compiler, which otherwise may
+// treat the descriptor as divergent and loop over the lanes at every load.
+__device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           kRsrcWord3);
+}
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct PrefillArgs {
   const uint8_t* planes;
@@ -57,160 +81,148 @@ struct PrefillArgs {
   const uint16_t* X;
   float* Y;
   int64_t M, K, N;
-  int bmax;
+  int m_tiles, halves;   // token tiles, 512-column halves of the store tiles
 };
 
-// Registers holding one step's global data for this thread.  Loads are
-// issued unconditionally from in-bounds addresses; what lies outside the
-// matrices is masked only when the data is consumed, so nothing waits for a
-// load before the next step.
+// One step's global data for this thread (raw; see the buffer-load notes).
 struct StepRegs {
-  u32x4_t x[kXChunks];      // X chunks (8 halves each)
-  uint32_t xok;             // bit u: chunk u lies inside X
-  uint32_t w1[8], w2[8];    // plane words of the thread's two rows (raw)
-  bool ok1, ok2;            // the two rows exist (row < K)
-  uint16_t s[2], z[2];      // scale and zero of the lane's two B-fragment columns
+  uint32_t x[kXChunks][4];   // X chunks: 8 halves each
+  uint32_t w1[8], w2[8];     // plane words of the thread's two rows
+  uint16_t s[2], z[2];       // scale and zero of the lane's two B-fragment columns
 };
-
-// Eight halves X[m][k .. k+7].  The address is clamped into the matrix;
-// `ok` says whether the chunk is real (the caller masks it later).  `aligned`
-// (K a multiple of 8, uniform) allows one 16-byte load per chunk; otherwise
-// the halves are loaded one by one and masked here (zeros outside X).
-__device__ inline u32x4_t load_x_chunk(const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t m,
-                                       int64_t k, bool aligned, bool& ok) {
-  const bool row_ok = m < M;
-  const int64_t mc = row_ok ? m : M - 1;
-  const uint16_t* row = X + mc * K;
-  u32x4_t v;
-  if (aligned) {
-    ok = row_ok && k < K;
-    v = *reinterpret_cast<const u32x4_t*>(row + (ok ? k : 0));
-  } else {
-    ok = true;
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const bool ok = row_ok && k + e < K;
-      const uint32_t val = row[ok ? k + e : 0];
-      h[e] = ok ? val : 0u;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = h[2 * e] | (h[2 * e + 1] << 16);
-  }
-  return v;
-}
 
 }  // namespace
 
+template <int BMAX>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kPM * kXPitch];
-  __shared__ __attribute__((aligned(16))) uint32_t s_w[kFrags * kPN * 4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_w[kFragRows * kPN * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wid >> 1, wc = wid & 1;
   const int64_t M = a.M, K = a.K, N = a.N;
-  const int64_t n0 = (int64_t)blockIdx.x * kPN;
-  const int64_t m0 = (int64_t)blockIdx.y * kPM;
-  const int64_t Np = padded_cols(N);
-  const int64_t t0 = n0 / kTile * kTile;                  // 1024-column tile of the store
-  const int ct = (int)((Np - t0) < kTile ? (Np - t0) : kTile);
-  const int pb = ct / 8;
-  const int word0 = (int)(n0 - t0) / 32;                  // first plane word of this column tile
-  const int bmax = a.bmax;
-  const int G = (int)n_groups(K);
 
-  // unpack unit of this thread: rows 2p, 2p + 1 of the step, plane word `uw`
-  const int up = tid & 63;
-  const int uw = tid >> 6;
+  // workgroup -> (token tile, column half); ids that share an XCD (id mod 8)
+  // take consecutive entries of the column-half-major order
+  const int T = a.m_tiles * a.halves;
+  int L = blockIdx.x;
+  if (T % kXCDs == 0) L = (L % kXCDs) * (T / kXCDs) + L / kXCDs;
+  const int half = L / a.m_tiles;
+  const int64_t m0 = (int64_t)(L % a.m_tiles) * kPM;
+  const int64_t t0 = (int64_t)(half >> 1) * kTile;      // store tile
+  const int64_t Np = padded_cols(N);
+  const int ct = (int)((Np - t0) < kTile ? (Np - t0) : kTile);
+  const int pb = __builtin_amdgcn_readfirstlane(ct / 8);   // uniform: used as a scalar offset
+  const int c0 = (half & 1) * kPN;                      // first column of this half in the tile
+  if (c0 >= ct) return;                                 // the half lies past a narrow last tile
+  const int steps = (int)((K + kPK - 1) / kPK);
+
+  // plane words: buffer over the store tile (row tiles of BMAX planes)
+  const uint32_t rstride = (uint32_t)(pb * BMAX);
+  const __amdgpu_buffer_rsrc_t prs = uniform_rsrc(a.planes + store_offset(t0 * K, BMAX), K * rstride);
+  // unpack unit: plane word uw (of this half) of rows 2 ur, 2 ur + 1 of the step
+  const int uw = tid & 15;
+  const int ur = tid >> 4;
+  const int word = c0 / 32 + uw;
+  const uint32_t wbyte = word < ct / 32 ? 4u * (uint32_t)word : kOOR;
+  // X: buffer over this tile's tokens; chunk c of this thread is token
+  // (tid + 512 c) / 8, halves 8 ((tid + 512 c) % 8) .. + 7 of the step
+  const int64_t mrows = (M - m0) < kPM ? (M - m0) : kPM;
+  const __amdgpu_buffer_rsrc_t xrs = uniform_rsrc(a.X + m0 * K, mrows * K * 2);
+  const bool x_even = (K & 1) == 0;
   // B-fragment columns of this lane (one per column block cb)
   int ncol[2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const int64_t n = n0 + 64 * wc + 32 * cb + (lane & 31);
+    const int64_t n = t0 + c0 + 64 * wid + 32 * cb + (lane & 31);
     ncol[cb] = (int)(n < N ? n : N - 1);
   }
 
-  const bool x_aligned = (K & 7) == 0;
-  auto load_step = [&](int g, StepRegs& r) {
-    const int64_t k0 = (int64_t)g * kPK;
-    r.xok = 0u;
+  auto load_step = [&](int st, StepRegs& r) {
+    const int64_t k0 = (int64_t)st * kPK;
 #pragma unroll
-    for (int u = 0; u < kXChunks; ++u) {
-      const int q = tid + u * kPThreads;
-      bool ok;
-      r.x[u] = load_x_chunk(a.X, M, K, m0 + (q >> 4), k0 + 8 * (q & 15), x_aligned, ok);
-      r.xok |= ok ? (1u << u) : 0u;
+    for (int c = 0; c < kXChunks; ++c) {
+      const int q = tid + c * kPThreads;
+      const int64_t k = k0 + 8 * (q & 7);
+      const uint32_t rowb = (uint32_t)((q >> 3) * K * 2);
+      if (x_even) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = k + 2 * e < K ? rowb + (uint32_t)(2 * (k + 2 * e)) : kOOR;
+          r.x[c][e] = __builtin_amdgcn_raw_buffer_load_b32(xrs, (int)off, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t o0 = k + 2 * e < K ? rowb + (uint32_t)(2 * (k + 2 * e)) : kOOR;
+          const uint32_t o1 = k + 2 * e + 1 < K ? rowb + (uint32_t)(2 * (k + 2 * e + 1)) : kOOR;
+          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(xrs, (int)o0, 0, 0);
+          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(xrs, (int)o1, 0, 0);
+          r.x[c][e] = lo | (hi << 16);
+        }
+      }
     }
-    // plane words: every load is in bounds (rows past K read row K - 1,
-    // planes past b_max read plane 0); masked when rebuilt
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int64_t row = k0 + 2 * up + e;
-      const bool ok = row < K;
+      const int64_t row = k0 + 2 * ur + e;
+      const uint32_t off = row < K ? (uint32_t)row * rstride + wbyte : kOOR;
       uint32_t* w = e == 0 ? r.w1 : r.w2;
-      (e == 0 ? r.ok1 : r.ok2) = ok;
-      const uint8_t* base = a.planes + store_offset(t0 * K + (ok ? row : K - 1) * ct, bmax) + 4 * (word0 + uw);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) w[p] = *reinterpret_cast<const uint32_t*>(base + (p < bmax ? p : 0) * pb);
+      for (int p = 0; p < BMAX; ++p) w[p] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, p * pb, 0);
+#pragma unroll
+      for (int p = BMAX; p < 8; ++p) w[p] = 0u;
     }
+    const int64_t g = k0 / kGroup;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      r.s[cb] = a.scales[(int64_t)g * N + ncol[cb]];
-      r.z[cb] = a.zeros[(int64_t)g * N + ncol[cb]];
+      r.s[cb] = a.scales[g * N + ncol[cb]];
+      r.z[cb] = a.zeros[g * N + ncol[cb]];
     }
   };
 
-  float16_t acc[2][2];
+  float16_t acc[4][2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
 
-  const int sh = 8 - bmax;                                   // codes come back as q 2^(8 - b_max)
-  const uint32_t keep = 0x01010101u * (0xFFu >> sh);
+  constexpr int kSh = 8 - BMAX;                              // codes come back as q 2^(8 - b_max)
+  constexpr uint32_t kKeep = 0x01010101u * (0xFFu >> kSh);
   StepRegs cur;
   load_step(0, cur);
-  for (int g = 0; g < G; ++g) {
-    // ---- X tile and rebuilt codes of this step into LDS
+  for (int st = 0; st < steps; ++st) {
+    // ---- X chunks and rebuilt codes of this step into LDS
 #pragma unroll
-    for (int u = 0; u < kXChunks; ++u) {
-      const int q = tid + u * kPThreads;
-      u32x4_t v = cur.x[u];
-      const bool ok = (cur.xok >> u) & 1u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = ok ? v[e] : 0u;
-      *reinterpret_cast<u32x4_t*>(&s_x[(q >> 4) * kXPitch + 8 * (q & 15)]) = v;
+    for (int c = 0; c < kXChunks; ++c) {
+      const int q = tid + c * kPThreads;
+      __builtin_memcpy(&s_x[(q >> 3) * kXPitch + 8 * (q & 7)], cur.x[c], 16);
     }
     {
-      uint32_t w1[8], w2[8], d1[8], d2[8];
+      uint32_t d1[8], d2[8];
+      planes_to_codes<BMAX>(cur.w1, d1);
+      planes_to_codes<BMAX>(cur.w2, d2);
+      if constexpr (kSh > 0) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        w1[p] = (cur.ok1 && p < bmax) ? cur.w1[p] : 0u;
-        w2[p] = (cur.ok2 && p < bmax) ? cur.w2[p] : 0u;
+        for (int m = 0; m < 8; ++m) {
+          d1[m] = (d1[m] >> kSh) & kKeep;
+          d2[m] = (d2[m] >> kSh) & kKeep;
+        }
       }
-      planes_to_codes<8>(w1, d1);
-      planes_to_codes<8>(w2, d2);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        d1[m] = (d1[m] >> sh) & keep;
-        d2[m] = (d2[m] >> sh) & keep;
-      }
-      const int kb = up >> 2, rr = up & 3;
+      const int kb = ur >> 2, rr = ur & 3;
       uint32_t* dst = s_w + (kb * kPN + 32 * uw) * 4 + rr;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // [row 2p code, 0x64, row 2p+1 code, 0x64] = fp16 (1024 + c1, 1024 + c2)
+          // [row 2r code, 0x64, row 2r+1 code, 0x64] = fp16 (1024 + c1, 1024 + c2)
           const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
           const uint32_t pr = __builtin_amdgcn_perm(d2[m], d1[m], sel) | 0x64006400u;
           const half2_t c = __builtin_bit_cast(half2_t, pr) - (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
           const int col = 4 * m + j;
-          dst[(col ^ kb) * 4] = __builtin_bit_cast(uint32_t, c);
+          dst[(col ^ uw) * 4] = __builtin_bit_cast(uint32_t, c);
         }
       }
     }
@@ -222,25 +234,20 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       z2[cb] = (uint32_t)cur.z[cb] * 0x00010001u;
     }
     __syncthreads();
-    if (g + 1 < G) load_step(g + 1, cur);
+    if (st + 1 < steps) load_step(st + 1, cur);
 
-    // ---- MFMAs over the step: 8 sub-steps of 16 rows
+    // ---- MFMAs over the step: 4 sub-steps of 16 rows
 #pragma unroll
     for (int s16 = 0; s16 < kPK / 16; ++s16) {
-      half8_t af[2], bf[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = 64 * wr + 32 * rb + (lane & 31);
-        af[rb] = *reinterpret_cast<const half8_t*>(&s_x[row * kXPitch + 16 * s16 + 8 * (lane >> 5)]);
-      }
+      half8_t af[4], bf[2];
       const int kb = 2 * s16 + (lane >> 5);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        const int nl = 64 * wc + 32 * cb;
-        // copied into a plain array: taking elements of the loaded vector
-        // inside a bit cast made this compiler read only the first dword
+        const int blk = 2 * wid + cb;   // 32-column block of the half
+        // copied into plain arrays: taking elements of a loaded vector inside
+        // a bit cast made this compiler read only the first dword
         uint32_t raw[4], wv[4];
-        __builtin_memcpy(raw, &s_w[(kb * kPN + nl + ((lane & 31) ^ kb)) * 4], 16);
+        __builtin_memcpy(raw, &s_w[(kb * kPN + 32 * blk + ((lane & 31) ^ blk)) * 4], 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           wv[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
@@ -250,7 +257,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         __builtin_memcpy(&bf[cb], wv, 16);
       }
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 4; ++rb) {
+        const int row = 32 * rb + (lane & 31);
+        __builtin_memcpy(&af[rb], &s_x[row * kXPitch + 16 * s16 + 8 * (lane >> 5)], 16);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
@@ -261,13 +273,13 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // ---- output: lane holds column (lane & 31) of each block, rows
   // 8 (v / 4) + 4 (lane / 32) + v % 4
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const int64_t n = n0 + 64 * wc + 32 * cb + (lane & 31);
+      const int64_t n = t0 + c0 + 64 * wid + 32 * cb + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + 64 * wr + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int64_t m = m0 + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m < M && n < N) a.Y[m * N + n] = acc[rb][cb][v];
       }
     }
@@ -275,11 +287,25 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 
 int launch_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros, const uint16_t* X,
                    int64_t M, int64_t K, int64_t N, int bmax, float* Y, hipStream_t s) {
+  // buffer ranges: one store tile (K 1024 b_max / 8 bytes) and one token
+  // tile of X (128 K 2 bytes) must stay below 2^31 bytes
+  if (K >= (int64_t(1) << 21))
+    return fail(GRINQH_EINVAL, "K = %lld: the prefill handles K < 2^21", (long long)K);
   const int64_t mt = (M + kPM - 1) / kPM;
-  const int64_t nt = (padded_cols(N) + kPN - 1) / kPN;
-  if (mt > 65535) return fail(GRINQH_EINVAL, "M = %lld: more than %d token tiles", (long long)M, 65535 * kPM);
-  PrefillArgs a{planes, scales, zeros, X, Y, M, K, N, bmax};
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)nt, (unsigned)mt), dim3(kPThreads), 0, s, a);
+  const int64_t nh = 2 * n_tiles(N);
+  if (mt * nh > 0x7FFFFFFF) return fail(GRINQH_EINVAL, "M x N needs more than 2^31 workgroups");
+  PrefillArgs a{planes, scales, zeros, X, Y, M, K, N, (int)mt, (int)nh};
+  const dim3 grid((unsigned)(mt * nh)), block(kPThreads);
+  switch (bmax) {
+    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(prefill_kernel<3>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL(prefill_kernel<5>, grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL(prefill_kernel<6>, grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL(prefill_kernel<7>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(prefill_kernel<8>, grid, block, 0, s, a); break;
+  }
   return check_launch("grinqh_prefill");
 }
 

@@ -206,8 +206,9 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
  * scales, zeros: fp16 [ceil(K/128)][N].
  * X:             fp16 [M][K] row-major (token m's activations in row m).
  * Y:             fp32 [M][N] row-major out (written completely).
- * Errors: EINVAL for NULL pointers, M, K, N <= 0, M or K or N >= 2^31,
- * b_max outside 1..8, or M above 65535 * 128.
+ * Errors: EINVAL for NULL pointers, M, K, N <= 0, M or N >= 2^31,
+ * K >= 2^21, b_max outside 1..8, or more than 2^31 - 1 workgroups
+ * (ceil(M / 128) x 2 ceil(N / 1024)).
  */
 int grinqh_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                    const uint16_t* X, int64_t M, int64_t K, int64_t N, int b_max, float* Y, void* stream);

@@ -164,4 +164,4 @@ def test_prefill_validation(lib):
     assert "M" in _err(lib)
     assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 4, 0, 64, 8, FAKE, None) == g.EINVAL
     assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 4, 128, 64, 9, FAKE, None) == g.EINVAL
-    assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 65535 * 128 + 1, 128, 64, 8, FAKE, None) == g.EINVAL
+    assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 4, 1 << 21, 64, 8, FAKE, None) == g.EINVAL
