@@ -31,11 +31,13 @@
 //   3. Each lane dequantises its B fragments right after reading them:
 //      w = s q + z with one packed fp16 fused multiply-add per two weights
 //      (one rounding to fp16); s and z are constant along a fragment.
-//   4. The next step's X, plane words, scales and zeros are loaded into
-//      registers while this step's MFMAs run.  Plane and X loads are buffer
-//      loads: rows past K, tokens past M, words past a narrow tile and
-//      columns past K read as zero through out-of-range offsets, and the
-//      plane index is a scalar offset.
+//   4. B is double-buffered in LDS: while a wave runs the MFMAs of one step
+//      it also rebuilds the codes of the next, and the two waves sharing a
+//      SIMD do the two in opposite order so that vector-ALU and matrix work
+//      overlap.  The step after that is loaded into registers meanwhile.
+//      Plane and X loads are buffer loads: rows past K, tokens past M, words
+//      past a narrow tile and columns past K read as zero through
+//      out-of-range offsets, and the plane index is a scalar offset.
 // Workgroups are numbered so that the ones sharing a column half land on the
 // same XCD (consecutive workgroup ids go to different XCDs), where they read
 // its planes through one L2.
@@ -96,12 +98,13 @@ struct StepRegs {
 template <int BMAX>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kPM * kXPitch];
-  __shared__ __attribute__((aligned(16))) uint32_t s_w[kFragRows * kPN * 4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_w[2][kFragRows * kPN * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t M = a.M, K = a.K, N = a.N;
+  const int64_t M = a.M, N = a.N;
+  const int K = (int)a.K;                               // < 2^21 (checked by the launcher)
 
   // workgroup -> (token tile, column half); ids that share an XCD (id mod 8)
   // take consecutive entries of the column-half-major order
@@ -116,11 +119,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   const int pb = __builtin_amdgcn_readfirstlane(ct / 8);   // uniform: used as a scalar offset
   const int c0 = (half & 1) * kPN;                      // first column of this half in the tile
   if (c0 >= ct) return;                                 // the half lies past a narrow last tile
-  const int steps = (int)((K + kPK - 1) / kPK);
+  const int steps = (K + kPK - 1) / kPK;
 
   // plane words: buffer over the store tile (row tiles of BMAX planes)
   const uint32_t rstride = (uint32_t)(pb * BMAX);
-  const __amdgpu_buffer_rsrc_t prs = uniform_rsrc(a.planes + store_offset(t0 * K, BMAX), K * rstride);
+  const __amdgpu_buffer_rsrc_t prs = uniform_rsrc(a.planes + store_offset(t0 * K, BMAX), (int64_t)K * rstride);
   // unpack unit: plane word uw (of this half) of rows 2 ur, 2 ur + 1 of the step
   const int uw = tid & 15;
   const int ur = tid >> 4;
@@ -140,12 +143,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   }
 
   auto load_step = [&](int st, StepRegs& r) {
-    const int64_t k0 = (int64_t)st * kPK;
+    const int k0 = st * kPK;
 #pragma unroll
     for (int c = 0; c < kXChunks; ++c) {
       const int q = tid + c * kPThreads;
-      const int64_t k = k0 + 8 * (q & 7);
-      const uint32_t rowb = (uint32_t)((q >> 3) * K * 2);
+      const int k = k0 + 8 * (q & 7);
+      const uint32_t rowb = (uint32_t)(q >> 3) * (uint32_t)K * 2u;
       if (x_even) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int64_t row = k0 + 2 * ur + e;
+      const int row = k0 + 2 * ur + e;
       const uint32_t off = row < K ? (uint32_t)row * rstride + wbyte : kOOR;
       uint32_t* w = e == 0 ? r.w1 : r.w2;
 #pragma unroll
@@ -181,6 +184,42 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     }
   };
 
+  constexpr int kSh = 8 - BMAX;                              // codes come back as q 2^(8 - b_max)
+  constexpr uint32_t kKeep = 0x01010101u * (0xFFu >> kSh);
+  // rebuilt codes of one step (plane words in r) into B buffer dst
+  auto unpack = [&](const StepRegs& r, uint32_t* buf) {
+    uint32_t d1[8], d2[8];
+    planes_to_codes<BMAX>(r.w1, d1);
+    planes_to_codes<BMAX>(r.w2, d2);
+    if constexpr (kSh > 0) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        d1[m] = (d1[m] >> kSh) & kKeep;
+        d2[m] = (d2[m] >> kSh) & kKeep;
+      }
+    }
+    uint32_t* dst = buf + ((ur >> 2) * kPN + 32 * uw) * 4 + (ur & 3);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // [row 2r code, 0x64, row 2r+1 code, 0x64] = fp16 (1024 + c1, 1024 + c2)
+        const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
+        const uint32_t pr = __builtin_amdgcn_perm(d2[m], d1[m], sel) | 0x64006400u;
+        const half2_t c = __builtin_bit_cast(half2_t, pr) - (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
+        const int col = 4 * m + j;
+        dst[(col ^ uw) * 4] = __builtin_bit_cast(uint32_t, c);
+      }
+    }
+  };
+  auto write_x = [&](const uint32_t (&x)[kXChunks][4]) {
+#pragma unroll
+    for (int c = 0; c < kXChunks; ++c) {
+      const int q = tid + c * kPThreads;
+      __builtin_memcpy(&s_x[(q >> 3) * kXPitch + 8 * (q & 7)], x[c], 16);
+    }
+  };
+
   float16_t acc[4][2];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
@@ -189,54 +228,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
 
-  constexpr int kSh = 8 - BMAX;                              // codes come back as q 2^(8 - b_max)
-  constexpr uint32_t kKeep = 0x01010101u * (0xFFu >> kSh);
-  StepRegs cur;
-  load_step(0, cur);
-  for (int st = 0; st < steps; ++st) {
-    // ---- X chunks and rebuilt codes of this step into LDS
-#pragma unroll
-    for (int c = 0; c < kXChunks; ++c) {
-      const int q = tid + c * kPThreads;
-      __builtin_memcpy(&s_x[(q >> 3) * kXPitch + 8 * (q & 7)], cur.x[c], 16);
-    }
-    {
-      uint32_t d1[8], d2[8];
-      planes_to_codes<BMAX>(cur.w1, d1);
-      planes_to_codes<BMAX>(cur.w2, d2);
-      if constexpr (kSh > 0) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          d1[m] = (d1[m] >> kSh) & kKeep;
-          d2[m] = (d2[m] >> kSh) & kKeep;
-        }
-      }
-      const int kb = ur >> 2, rr = ur & 3;
-      uint32_t* dst = s_w + (kb * kPN + 32 * uw) * 4 + rr;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // [row 2r code, 0x64, row 2r+1 code, 0x64] = fp16 (1024 + c1, 1024 + c2)
-          const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
-          const uint32_t pr = __builtin_amdgcn_perm(d2[m], d1[m], sel) | 0x64006400u;
-          const half2_t c = __builtin_bit_cast(half2_t, pr) - (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
-          const int col = 4 * m + j;
-          dst[(col ^ uw) * 4] = __builtin_bit_cast(uint32_t, c);
-        }
-      }
-    }
-    // scale and zero of this step, duplicated into both halves
-    uint32_t s2[2], z2[2];
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      s2[cb] = (uint32_t)cur.s[cb] * 0x00010001u;
-      z2[cb] = (uint32_t)cur.z[cb] * 0x00010001u;
-    }
-    __syncthreads();
-    if (st + 1 < steps) load_step(st + 1, cur);
-
-    // ---- MFMAs over the step: 4 sub-steps of 16 rows
+  // MFMAs of one step from B buffer buf; s2, z2: scale and zero pairs
+  auto mfma_step = [&](const uint32_t* buf, const uint32_t (&s2)[2], const uint32_t (&z2)[2]) {
 #pragma unroll
     for (int s16 = 0; s16 < kPK / 16; ++s16) {
       half8_t af[4], bf[2];
@@ -247,7 +240,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         // copied into plain arrays: taking elements of a loaded vector inside
         // a bit cast made this compiler read only the first dword
         uint32_t raw[4], wv[4];
-        __builtin_memcpy(raw, &s_w[(kb * kPN + 32 * blk + ((lane & 31) ^ blk)) * 4], 16);
+        __builtin_memcpy(raw, &buf[(kb * kPN + 32 * blk + ((lane & 31) ^ blk)) * 4], 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           wv[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(
@@ -267,7 +260,54 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         for (int cb = 0; cb < 2; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
     }
-    __syncthreads();
+  };
+
+  // ---- software pipeline.  B is double-buffered: during step st every wave
+  // runs the MFMAs of step st and rebuilds the codes of step st + 1 into the
+  // other buffer.  The two waves that share a SIMD (w and w + 4) do the two
+  // halves in opposite order, so one's vector-ALU work overlaps the other's
+  // matrix work.  X is single-buffered and rewritten between two barriers.
+  StepRegs r;
+  uint32_t s2[2], z2[2], xn[kXChunks][4];
+  load_step(0, r);
+  unpack(r, s_w[0]);
+  write_x(r.x);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    s2[cb] = (uint32_t)r.s[cb] * 0x00010001u;
+    z2[cb] = (uint32_t)r.z[cb] * 0x00010001u;
+  }
+  if (steps > 1) load_step(1, r);
+  __syncthreads();
+  const bool matrix_first = wid >= kPWaves / 2;
+  for (int st = 0; st < steps; ++st) {
+    const bool more = st + 1 < steps;
+    const uint32_t* cur = s_w[st & 1];
+    uint32_t* nxt = s_w[(st + 1) & 1];
+    if (matrix_first) mfma_step(cur, s2, z2);
+    if (more) {
+      unpack(r, nxt);
+#pragma unroll
+      for (int c = 0; c < kXChunks; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xn[c][e] = r.x[c][e];
+    }
+    uint32_t s2n[2], z2n[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      s2n[cb] = (uint32_t)r.s[cb] * 0x00010001u;
+      z2n[cb] = (uint32_t)r.z[cb] * 0x00010001u;
+    }
+    if (st + 2 < steps) load_step(st + 2, r);
+    if (!matrix_first) mfma_step(cur, s2, z2);
+    __syncthreads();                 // MFMAs of st done with X; codes of st + 1 written
+    if (more) write_x(xn);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      s2[cb] = s2n[cb];
+      z2[cb] = z2n[cb];
+    }
+    __syncthreads();                 // X of st + 1 visible
   }
 
   // ---- output: lane holds column (lane & 31) of each block, rows
