@@ -10,4 +10,5 @@ from .grinqh_oracle import (  # noqa: F401
     padded_cols, tiles, planes_bytes, plane_offset, pack, read_planes, span_bytes,
     reconstruct_level, vmm, vmm_abs, decode_step, bytes_read,
     dequant_dense, prefill, prefill_abs,
+    vmm_lut, vmm_lut_abs,
 )

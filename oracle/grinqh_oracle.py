@@ -324,6 +324,60 @@ def decode_step(codes, scales, zeros, x, thresholds, levels, b_max: int = B_MAX)
 
 
 # --------------------------------------------------------------------------
+# Non-uniform nested weights with look-up tables -- section 3.3 "Storage
+# Layout and Weight Loading" (k-means style nested codes: the parent is
+# quantised at b_max bits and every prefix of a code names a coarser level)
+# and "Weight Reconstruction and Bias Correction" (with LUTs the nested
+# levels are already centred, so there is no midpoint term); Appendix E.2
+# (any-precision nested weights).
+#
+# Reading: one table per output column and bit width, as the nested
+# k-means formats cited there keep one per output channel; row i at width b
+# reads entry (q_ij >> (b_max - b)) of column j's b-bit table.  Tables are
+# passed as lut[b] = array [N][2^b] for b = 1..b_max (lut[0] unused).
+# --------------------------------------------------------------------------
+
+def vmm_lut(codes, lut, x, bits, b_max: int = B_MAX) -> np.ndarray:
+    """y_j = sum over rows with b_i > 0 of x_i * lut[b_i][j][prefix], fp64.
+
+    prefix = floor(q_ij / 2^(b_max - b_i)), the top b_i bits of the code;
+    rows with b_i = 0 are bypassed.  Table entries enter as given (fp16
+    values are exact in fp64).
+    """
+    b_max = _check_bmax(b_max)
+    codes = np.asarray(codes, dtype=np.int64)
+    K, N = codes.shape
+    x64 = np.asarray(x, dtype=np.float16).astype(np.float64)
+    bits = np.asarray(bits)
+    cols = np.arange(N)
+    y = np.zeros(N, dtype=np.float64)
+    for i in np.nonzero(bits > 0)[0]:
+        b = int(bits[i])
+        if b > b_max:
+            raise ValueError(f"row {i}: width {b} above b_max = {b_max}")
+        prefix = codes[i] // (1 << (b_max - b))
+        table = np.asarray(lut[b], dtype=np.float64)
+        y += x64[i] * table[cols, prefix]
+    return y
+
+
+def vmm_lut_abs(codes, lut, x, bits, b_max: int = B_MAX) -> np.ndarray:
+    """sum_i |x_i * w_hat_ij| for the LUT reconstruction (tolerance scale)."""
+    b_max = _check_bmax(b_max)
+    codes = np.asarray(codes, dtype=np.int64)
+    K, N = codes.shape
+    x64 = np.abs(np.asarray(x, dtype=np.float16).astype(np.float64))
+    bits = np.asarray(bits)
+    cols = np.arange(N)
+    out = np.zeros(N, dtype=np.float64)
+    for i in np.nonzero(bits > 0)[0]:
+        b = int(bits[i])
+        prefix = codes[i] // (1 << (b_max - b))
+        out += x64[i] * np.abs(np.asarray(lut[b], dtype=np.float64)[cols, prefix])
+    return out
+
+
+# --------------------------------------------------------------------------
 # Dense prefill -- section 3 (the prefill stage loads weights at a fixed
 # precision), section 4 "Prefill vs. Decoding Evaluation" (the kernel unpacks
 # the weights at full b_max precision and multiplies densely) and section 5

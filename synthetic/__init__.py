@@ -171,6 +171,57 @@ def make_activations(K: int, count: int, config: int = 0, matrix: int = 0,
     return x.astype(np.float16)
 
 
+def lut_offsets(N: int, b_max: int = 8) -> list:
+    """Start of each width's block in the flat LUT buffer (index b; [0] unused).
+
+    Blocks for b = 1..b_max follow each other; block b holds N tables of 2^b
+    fp16 entries (column j's table at j 2^b), so it starts at N (2^b - 2).
+    """
+    return [0] + [N * ((1 << b) - 2) for b in range(1, b_max + 1)]
+
+
+def lut_flat(tables, N: int, b_max: int = 8) -> np.ndarray:
+    """Per-width tables (tables[b] = fp16 [N][2^b]) -> one flat fp16 buffer."""
+    out = np.zeros(N * ((1 << (b_max + 1)) - 2), dtype=np.float16)
+    off = lut_offsets(N, b_max)
+    for b in range(1, b_max + 1):
+        t = np.asarray(tables[b], dtype=np.float16)
+        if t.shape != (N, 1 << b):
+            raise ValueError(f"table {b} has shape {t.shape}, expected {(N, 1 << b)}")
+        out[off[b]:off[b] + N * (1 << b)] = t.reshape(-1)
+    return out
+
+
+def make_lut_weights(K: int, N: int, config: int = 0, matrix: int = 0, b_max: int = 8):
+    """Nested non-uniform codes with one table per output column and width.
+
+    Stands in for a k-means style nested quantiser (the pages cite one):
+    column j's weights are N(0, sigma_j^2) with sigma_j = 0.02 (0.5 + u_j);
+    its b_max-bit centroids sit at the normal quantiles (c + 1/2) / 2^b_max
+    times sigma_j, a code is the index of the nearest centroid, and the
+    b-bit table entry of prefix p is the mean of the b_max-bit centroids
+    whose codes start with p (each coarser level centred on its children).
+    Tables are rounded to fp16.  Returns (codes u8 [K][N], tables) with
+    tables[b] fp16 [N][2^b] for b = 1..b_max (tables[0] = None).
+    """
+    from scipy.special import ndtri
+    r = rng(config, matrix, ROLE_W)
+    sigma = WEIGHT_STD * (0.5 + r.random(N))
+    L = 1 << b_max
+    base = ndtri((np.arange(L) + 0.5) / L)                     # sorted
+    mids = (base[1:] + base[:-1]) / 2.0
+    codes = np.empty((K, N), dtype=np.uint8)
+    for g0 in range(0, K, GROUP):
+        rows = min(GROUP, K - g0)
+        z = r.standard_normal((rows, N))                       # w / sigma_j
+        codes[g0:g0 + rows] = np.searchsorted(mids, z).astype(np.uint8)
+    parent = sigma[:, None] * base[None, :]                    # fp64 [N][L]
+    tables = [None] * (b_max + 1)
+    for b in range(1, b_max + 1):
+        tables[b] = parent.reshape(N, 1 << b, L >> b).mean(axis=2).astype(np.float16)
+    return codes, tables
+
+
 def make_calibration(K: int, config: int = 0, matrix: int = 0, count: int = N_CALIB) -> np.ndarray:
     return make_activations(K, count, config, matrix, ROLE_CALIB)
 
