@@ -9,7 +9,7 @@ call raises.
 
 Names follow the C ABI in ``include/grinqh.h``:
 ``pack``, ``calibrate``, ``assign_bits``, ``vmm``, ``decode_vmm``,
-``decode_vmm_accumulate``, ``prefill``.
+``decode_vmm_accumulate``, ``decode_vmm_lut``, ``prefill``.
 """
 from __future__ import annotations
 
@@ -58,6 +58,8 @@ _SIGNATURES = {
     "grinqh_decode_vmm_accumulate": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp],
                                      _i32),
     "grinqh_prefill": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
+    "grinqh_lut_entries": ([_i64, _i32], _i64),
+    "grinqh_decode_vmm_lut": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
 }
 
 
@@ -260,3 +262,27 @@ def prefill(planes, scales, zeros, X, K: int, N: int, out=None, stream=None, b_m
         planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), X.data_ptr(), M, K, N, b_max,
         out.data_ptr(), _stream(stream)))
     return out
+
+
+def lut_entries(N: int, b_max: int = MAX_BITS) -> int:
+    n = lib().grinqh_lut_entries(N, b_max)
+    if n < 0:
+        raise ValueError(f"no table buffer for N = {N}, b_max = {b_max}")
+    return n
+
+
+def decode_vmm_lut(planes, lut, x, K: int, N: int, thresholds: Sequence[float], levels: Sequence[int], y,
+                   clear=None, stream=None, b_max: int = MAX_BITS):
+    """y += the decode step with table reconstruction (fp32 atomics); zeroes `clear` if given."""
+    import torch
+    _dev(planes, "planes", torch.uint8, (planes_bytes(K, N, b_max),))
+    _dev(lut, "lut", torch.float16, (lut_entries(N, b_max),))
+    _dev(x, "x", torch.float16, (K,))
+    _dev(y, "y", torch.float32, (N,))
+    if clear is not None:
+        _dev(clear, "clear", torch.float32, (N,))
+    th, lv, n = _host_thresholds(thresholds, levels)
+    _check("grinqh_decode_vmm_lut", lib().grinqh_decode_vmm_lut(
+        planes.data_ptr(), lut.data_ptr(), x.data_ptr(), K, N, b_max, ctypes.cast(th, _vp), ctypes.cast(lv, _vp),
+        n, y.data_ptr(), clear.data_ptr() if clear is not None else None, _stream(stream)))
+    return y

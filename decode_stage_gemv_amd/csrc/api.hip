@@ -199,6 +199,29 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
   return launch_vmm_accumulate(planes, scales, zeros, x, K, N, b_max, ap, y, clear, as_stream(stream));
 }
 
+int64_t grinqh_lut_entries(int64_t N, int b_max) {
+  if (N <= 0 || b_max < 1 || b_max > GRINQH_MAX_BITS) return -1;
+  return N * ((int64_t(1) << (b_max + 1)) - 2);
+}
+
+int grinqh_decode_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x, int64_t K, int64_t N,
+                          int b_max, const float* thresholds, const uint8_t* levels, int n, float* y,
+                          float* clear, void* stream) {
+  g_last_error[0] = 0;
+  if (!lut) return fail(GRINQH_EINVAL, "NULL data pointer");
+  int st = check_layer(planes, lut, lut, x, y, K, N, b_max);
+  if (st != GRINQH_OK) return st;
+  if (clear) {
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(clear), y0 = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t len = (uintptr_t)N * sizeof(float);
+    if (c0 < y0 + len && y0 < c0 + len) return fail(GRINQH_EINVAL, "clear overlaps y");
+  }
+  AssignParams ap;
+  st = check_assign_params(thresholds, levels, n, b_max, &ap);
+  if (st != GRINQH_OK) return st;
+  return launch_vmm_lut(planes, lut, x, K, N, b_max, ap, y, clear, as_stream(stream));
+}
+
 int grinqh_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                    const uint16_t* X, int64_t M, int64_t K, int64_t N, int b_max, float* Y, void* stream) {
   g_last_error[0] = 0;

@@ -97,6 +97,8 @@ int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const u
                           float* y, float* clear, hipStream_t s);
 int launch_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros, const uint16_t* X,
                    int64_t M, int64_t K, int64_t N, int bmax, float* Y, hipStream_t s);
+int launch_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x, int64_t K, int64_t N,
+                   int bmax, const AssignParams& ap, float* y, float* clear, hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 }  // namespace grinqh

@@ -194,6 +194,38 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
                                  float* y, float* clear, void* stream);
 
 /*
+ * Look-up-table reconstruction of nested non-uniform weights (section 3.3:
+ * k-means style nested codes in the same bit-plane store, and with tables
+ * the nested levels are already centred, so no midpoint term; Appendix E.2).
+ * Column j has one fp16 table per width b = 1..b_max with 2^b entries; row i
+ * at width b_i reads entry (q_ij >> (b_max - b_i)) of column j's b_i-bit
+ * table.  The flat table buffer holds, for b = 1, 2, ..., b_max in turn, a
+ * block of N tables of 2^b entries (column j's at j 2^b), so block b starts
+ * at entry N (2^b - 2); grinqh_lut_entries(N, b_max) = N (2^(b_max+1) - 2)
+ * entries in all.  Returns -1 for N <= 0 or b_max outside 1..8.
+ */
+int64_t grinqh_lut_entries(int64_t N, int b_max);
+
+/*
+ * Accumulating decode step with table reconstruction (sections 3.1 and 3.3):
+ *   y[j] += sum over i with b_i > 0 of x_i T_{b_i}[j][q_ij >> (b_max - b_i)],
+ * b_i from |x_i| and the thresholds as in grinqh_assign_bits.  Only the top
+ * b_i planes of a row are read; only the tables of the levels in use are
+ * read.  Sums are fp32, added into y with fp32 device-scope atomics (the
+ * order of the additions is not fixed).
+ * planes:  the store (layout above) of the b_max-bit parent codes.
+ * lut:     fp16 [grinqh_lut_entries(N, b_max)], layout above.
+ * x:       fp16 [K].  thresholds, levels, n: as in grinqh_assign_bits, levels
+ *          at most b_max.
+ * y:       fp32 [N], read and updated.  clear: fp32 [N] or NULL, set to zero
+ *          by this call (it must not overlap y).
+ * Errors: as grinqh_decode_vmm_accumulate, and EINVAL for a NULL table.
+ */
+int grinqh_decode_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x, int64_t K, int64_t N,
+                          int b_max, const float* thresholds, const uint8_t* levels, int n, float* y,
+                          float* clear, void* stream);
+
+/*
  * Dense prefill of a batch of M tokens (section 3: the prefill stage loads
  * weights at one fixed precision; section 4 "Prefill vs. Decoding
  * Evaluation": weights are unpacked at full b_max precision and multiplied
