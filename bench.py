@@ -302,6 +302,57 @@ def prefill_bench(layer, M, steps=20, warmup=3, dense_reference=True):
     return out
 
 
+def lut_bench(name, steps=100, warmup=10):
+    """grinqh_decode_vmm_lut on the workload's shape with nested synthetic
+    tables (one per output column and width), decode-loop ping-pong outputs,
+    rotated copies of planes, tables and x so the working set exceeds the
+    Infinity Cache.  Algorithmic bytes per step: the planes the rows' widths
+    select, the tables of the levels in use (N 2^b fp16 entries per width)
+    and x."""
+    import torch
+    import synthetic
+    import decode_stage_gemv_amd as grq
+    K, N, cfg, mat, pkey, lv = WORKLOADS[name]
+    P, levels = _P(pkey, lv)
+    b_max = bmax_of(lv)
+    t_setup = time.time()
+    codes, tables = synthetic.make_lut_weights(K, N, config=cfg, matrix=mat, b_max=b_max)
+    dev = torch.device("cuda:0")
+    planes = grq.pack(torch.from_numpy(codes).to(dev), b_max=b_max)
+    lut = torch.from_numpy(synthetic.lut_flat(tables, N, b_max)).to(dev)
+    calib = torch.from_numpy(synthetic.make_calibration(K, config=cfg, matrix=mat)).to(dev)
+    th = [float(v) for v in grq.calibrate(calib, P).cpu().numpy()]
+    per_copy = planes.numel() + 2 * lut.numel() + 2 * K
+    R = max(1, -(-ROT_BYTES // per_copy))
+    xs = synthetic.make_activations(K, R, config=cfg, matrix=mat)
+    copies = [(planes if r == 0 else planes.clone(), lut if r == 0 else lut.clone(),
+               torch.from_numpy(xs[r]).to(dev)) for r in range(R)]
+    ybufs = [torch.zeros(N, dtype=torch.float32, device=dev) for _ in range(2)]
+    used = sorted(set(int(v) for v in levels if v > 0))
+    lut_bytes = sum(N * (1 << b) * 2 for b in used)
+    step_bytes = []
+    np_cols = int(grq.lib().grinqh_planes_bytes(1, N, 8))
+    for (_, _, x) in copies:
+        bits, _, _ = grq.assign_bits(x, th, levels)
+        step_bytes.append(int(bits.to(torch.int64).sum().item()) * np_cols // 8 + lut_bytes + 2 * K)
+    state = {"k": 0}
+
+    def step():
+        k = state["k"]
+        state["k"] += 1
+        pl, lt, x = copies[k % R]
+        grq.decode_vmm_lut(pl, lt, x, K, N, th, levels, ybufs[k % 2], ybufs[(k + 1) % 2], b_max=b_max)
+
+    log(f"lut layer {K}x{N} (b_max {b_max}): R={R} copies, setup {time.time() - t_setup:.1f}s")
+    us = _graph_time(step, steps, warmup)
+    b = float(np.mean([step_bytes[k % R] for k in range(steps)]))
+    out = {"workload": name, "entry_point": "grinqh_decode_vmm_lut", "us_per_vmm": us,
+           "GB_s": b / (us * 1e-6) / 1e9, "bytes_per_step": b, "table_bytes_per_step": lut_bytes}
+    out["frac_of_peak"] = out["GB_s"] / HBM_PEAK_GBS
+    log(f"{name} grinqh_decode_vmm_lut: {us:.2f} us/VMM, {out['GB_s']:.1f} GB/s ({out['frac_of_peak']:.1%})")
+    return out
+
+
 def copy_probe(nbytes=512 << 20, reps=20):
     """A plain device-to-device copy of known size: reads nbytes, writes nbytes."""
     import torch
@@ -377,6 +428,9 @@ def main():
                     help="tokens of the dense prefill timed on the same layer (0: skip)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the dense prefill of the chosen workload's layer")
+    ap.add_argument("--no-lut", action="store_true",
+                    help="skip the table-reconstruction leg (grinqh_decode_vmm_lut)")
+    ap.add_argument("--lut-only", action="store_true", help="time only grinqh_decode_vmm_lut")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode VMM path runs on a single GPU "
@@ -389,6 +443,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.lut_only:
+        print(json.dumps({"lut": lut_bench(args.workload, min(args.steps, 100), min(args.warmup, 10))}), flush=True)
         return
     if args.prefill_only:
         K, N, cfg, mat, _, lv = WORKLOADS[args.workload]
@@ -442,6 +499,9 @@ def main():
     prefill = None
     if args.prefill_tokens > 0 and not args.only:
         prefill = prefill_bench(prep.layer, args.prefill_tokens)
+    lut = None
+    if not args.no_lut and not args.only:
+        lut = lut_bench(args.workload, min(args.steps, 100), min(args.warmup, 10))
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(prep)
     traffic = measured_traffic(args.workload, args.mode)
@@ -476,6 +536,8 @@ def main():
         out["sweep"] = sweep
     if prefill:
         out["prefill"] = prefill
+    if lut:
+        out["lut"] = lut
     print(json.dumps(out), flush=True)
 
 
