@@ -9,7 +9,8 @@ call raises.
 
 Names follow the C ABI in ``include/grinqh.h``:
 ``pack``, ``calibrate``, ``assign_bits``, ``vmm``, ``decode_vmm``,
-``decode_vmm_accumulate``, ``decode_vmm_lut``, ``prefill``.
+``decode_vmm_accumulate``, ``decode_vmm_lut``, ``prefill``, ``unpack_dense``,
+``dense_gemm``.
 """
 from __future__ import annotations
 
@@ -59,6 +60,9 @@ _SIGNATURES = {
                                      _i32),
     "grinqh_prefill": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
     "grinqh_lut_entries": ([_i64, _i32], _i64),
+    "grinqh_dense_bytes": ([_i64, _i64], _i64),
+    "grinqh_unpack_dense": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp], _i32),
+    "grinqh_dense_gemm": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "grinqh_decode_vmm_lut": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
 }
 
@@ -286,3 +290,39 @@ def decode_vmm_lut(planes, lut, x, K: int, N: int, thresholds: Sequence[float], 
         planes.data_ptr(), lut.data_ptr(), x.data_ptr(), K, N, b_max, ctypes.cast(th, _vp), ctypes.cast(lv, _vp),
         n, y.data_ptr(), clear.data_ptr() if clear is not None else None, _stream(stream)))
     return y
+
+
+def dense_bytes(K: int, N: int) -> int:
+    return lib().grinqh_dense_bytes(K, N)
+
+
+def unpack_dense(planes, scales, zeros, K: int, N: int, out=None, stream=None, b_max: int = MAX_BITS):
+    """The store at full width as dense fp16 weights in B-fragment order (u8 buffer)."""
+    import torch
+    _dev(planes, "planes", torch.uint8, (planes_bytes(K, N, b_max),))
+    _dev(scales, "scales", torch.float16, (n_groups(K), N))
+    _dev(zeros, "zeros", torch.float16, (n_groups(K), N))
+    nbytes = dense_bytes(K, N)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=planes.device) if out is None else out
+    _dev(out, "dense", torch.uint8)
+    _check("grinqh_unpack_dense", lib().grinqh_unpack_dense(
+        planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), K, N, b_max, out.data_ptr(), out.numel(),
+        _stream(stream)))
+    return out
+
+
+def dense_gemm(X, dense, K: int, N: int, out=None, stream=None):
+    """Y fp32 [M][N] = X fp16 [M][K] times the unpacked weights in `dense`."""
+    import torch
+    _dev(X, "X", torch.float16)
+    if X.dim() != 2 or X.shape[1] != K:
+        raise ValueError(f"X must be [M][{K}], got {tuple(X.shape)}")
+    M = X.shape[0]
+    _dev(dense, "dense", torch.uint8)
+    if dense.numel() < dense_bytes(K, N):
+        raise ValueError("dense buffer too small")
+    out = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _dev(out, "Y", torch.float32, (M, N))
+    _check("grinqh_dense_gemm", lib().grinqh_dense_gemm(X.data_ptr(), dense.data_ptr(), M, K, N, out.data_ptr(),
+                                                        _stream(stream)))
+    return out

@@ -222,6 +222,32 @@ int grinqh_decode_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint
   return launch_vmm_lut(planes, lut, x, K, N, b_max, ap, y, clear, as_stream(stream));
 }
 
+int64_t grinqh_dense_bytes(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0) return -1;
+  return unpack_dense_bytes(K, N);
+}
+
+int grinqh_unpack_dense(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros, int64_t K,
+                        int64_t N, int b_max, void* dense, size_t dense_bytes, void* stream) {
+  g_last_error[0] = 0;
+  int st = check_layer(planes, scales, zeros, dense, dense, K, N, b_max);
+  if (st != GRINQH_OK) return st;
+  if ((int64_t)dense_bytes < unpack_dense_bytes(K, N))
+    return fail(GRINQH_EINVAL, "dense buffer has %zu bytes, needs %lld", dense_bytes, (long long)unpack_dense_bytes(K, N));
+  if (reinterpret_cast<uintptr_t>(dense) % 16 != 0) return fail(GRINQH_EINVAL, "dense buffer must be 16-byte aligned");
+  return launch_unpack_dense(planes, scales, zeros, K, N, b_max, dense, as_stream(stream));
+}
+
+int grinqh_dense_gemm(const uint16_t* X, const void* dense, int64_t M, int64_t K, int64_t N, float* Y, void* stream) {
+  g_last_error[0] = 0;
+  if (!X || !dense || !Y) return fail(GRINQH_EINVAL, "NULL data pointer");
+  if (M <= 0 || M >= (int64_t(1) << 31)) return fail(GRINQH_EINVAL, "M = %lld out of range", (long long)M);
+  int st = check_shape(K, N, 8);
+  if (st != GRINQH_OK) return st;
+  if (reinterpret_cast<uintptr_t>(dense) % 16 != 0) return fail(GRINQH_EINVAL, "dense buffer must be 16-byte aligned");
+  return launch_dense_gemm(X, dense, M, K, N, Y, as_stream(stream));
+}
+
 int grinqh_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                    const uint16_t* X, int64_t M, int64_t K, int64_t N, int b_max, float* Y, void* stream) {
   g_last_error[0] = 0;

@@ -99,6 +99,13 @@ int launch_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t
                    int64_t M, int64_t K, int64_t N, int bmax, float* Y, hipStream_t s);
 int launch_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x, int64_t K, int64_t N,
                    int bmax, const AssignParams& ap, float* y, float* clear, hipStream_t s);
+// rows of the unpacked dense weights: K padded to a multiple of 64 (one
+// K-step of the dense GEMM) so that the GEMM's loads need no bounds checks
+__host__ __device__ inline int64_t dense_rows(int64_t K) { return (K + 63) / 64 * 64; }
+int64_t unpack_dense_bytes(int64_t K, int64_t N);
+int launch_unpack_dense(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros, int64_t K,
+                        int64_t N, int bmax, void* out, hipStream_t s);
+int launch_dense_gemm(const uint16_t* X, const void* W, int64_t M, int64_t K, int64_t N, float* Y, hipStream_t s);
 int launch_fill_zero(void* ptr, size_t bytes, hipStream_t s);
 
 }  // namespace grinqh

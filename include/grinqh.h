@@ -245,6 +245,36 @@ int grinqh_decode_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint
 int grinqh_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                    const uint16_t* X, int64_t M, int64_t K, int64_t N, int b_max, float* Y, void* stream);
 
+/*
+ * Unpacked prefill, first half: the store at full width as dense fp16
+ * weights (section 4 "Prefill vs. Decoding Evaluation": weights unpacked at
+ * full b_max precision for a dense product; section 3.3: w = s q + z, nothing
+ * truncated at b_max), each rounded once to the nearest fp16.
+ * Layout ("B-fragment order"): w[k][n] at fp16 index ((k / 8) N_pad + n) 8 +
+ * k % 8, where N_pad = N rounded up to 128: eight consecutive rows of a column
+ * are one 16-byte fragment.  Rows past K, up to K_pad = K rounded up to 64,
+ * and columns past N are 0.
+ * grinqh_dense_bytes(K, N) = K_pad N_pad 2 bytes (-1 for K, N <= 0).
+ * dense: device buffer of at least that size, 16-byte aligned, written
+ * completely.  Unpacking once lets several token batches share it (the buffer
+ * costs 2 bytes per weight while it lives).
+ * Errors: as grinqh_pack, and EINVAL for a NULL, misaligned or small buffer.
+ */
+int64_t grinqh_dense_bytes(int64_t K, int64_t N);
+int grinqh_unpack_dense(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros, int64_t K,
+                        int64_t N, int b_max, void* dense, size_t dense_bytes, void* stream);
+
+/*
+ * Unpacked prefill, second half: Y fp32 [M][N] = X fp16 [M][K] times the
+ * weights in `dense` (from grinqh_unpack_dense for the same K, N), products
+ * summed in fp32 on the matrix cores.  Together the two calls compute what
+ * grinqh_prefill computes (same fp16 weight rounding), trading a 2-byte-per-
+ * weight buffer for a plain matrix product.
+ * Errors: EINVAL for NULL pointers, M, K, N <= 0, M or N >= 2^31, K >= 2^21,
+ * or a misaligned buffer.
+ */
+int grinqh_dense_gemm(const uint16_t* X, const void* dense, int64_t M, int64_t K, int64_t N, float* Y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

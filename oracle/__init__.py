@@ -9,6 +9,6 @@ from .grinqh_oracle import (  # noqa: F401
     assign, compact,
     padded_cols, tiles, planes_bytes, plane_offset, pack, read_planes, span_bytes,
     reconstruct_level, vmm, vmm_abs, decode_step, bytes_read,
-    dequant_dense, prefill, prefill_abs,
+    dequant_dense, dequant_dense_fp16, prefill, prefill_abs,
     vmm_lut, vmm_lut_abs,
 )

@@ -396,6 +396,15 @@ def dequant_dense(codes, scales, zeros, b_max: int = B_MAX) -> np.ndarray:
     return _dequant_rows(codes, scales, zeros, rows, np.full(K, _check_bmax(b_max)), b_max)
 
 
+def dequant_dense_fp16(codes, scales, zeros, b_max: int = B_MAX) -> np.ndarray:
+    """The dense weights rounded once to fp16 (round to nearest even).
+
+    s q + z is exact in fp64 for fp16 s, z and an 8-bit q, so this is the
+    correctly rounded fp16 value of each weight.
+    """
+    return dequant_dense(codes, scales, zeros, b_max).astype(np.float16)
+
+
 def prefill(codes, scales, zeros, X, b_max: int = B_MAX) -> np.ndarray:
     """Y = X W_hat in fp64 for a batch of M token activations X fp16 [M][K]."""
     X64 = np.asarray(X, dtype=np.float16).astype(np.float64)

@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
         assert name in g._SIGNATURES, name
@@ -165,3 +165,17 @@ def test_prefill_validation(lib):
     assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 4, 0, 64, 8, FAKE, None) == g.EINVAL
     assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 4, 128, 64, 9, FAKE, None) == g.EINVAL
     assert lib.grinqh_prefill(FAKE, FAKE, FAKE, FAKE, 4, 1 << 21, 64, 8, FAKE, None) == g.EINVAL
+
+
+def test_unpacked_prefill_validation(lib):
+    assert lib.grinqh_dense_bytes(4096, 14336) == 512 * 14336 * 16
+    assert lib.grinqh_dense_bytes(9, 33) == 64 * 128 * 2       # rows padded to 64, columns to 128
+    assert lib.grinqh_dense_bytes(0, 4) == -1
+    need = lib.grinqh_dense_bytes(64, 64)
+    assert lib.grinqh_unpack_dense(FAKE, FAKE, FAKE, 64, 64, 8, FAKE, need - 1, None) == g.EINVAL
+    assert lib.grinqh_unpack_dense(FAKE, FAKE, FAKE, 64, 64, 8, FAKE + 8, need, None) == g.EINVAL
+    assert "aligned" in _err(lib)
+    assert lib.grinqh_unpack_dense(FAKE, FAKE, FAKE, 64, 64, 0, FAKE, need, None) == g.EINVAL
+    assert lib.grinqh_dense_gemm(FAKE, FAKE, 0, 64, 64, FAKE, None) == g.EINVAL
+    assert lib.grinqh_dense_gemm(FAKE, FAKE, 4, 1 << 21, 64, FAKE, None) == g.EINVAL
+    assert lib.grinqh_dense_gemm(None, FAKE, 4, 64, 64, FAKE, None) == g.EINVAL

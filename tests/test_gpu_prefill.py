@@ -119,3 +119,53 @@ def test_prefill_full_size_sampled(M, K, N, cfg, mat, b_max):
     rows = np.unique(np.concatenate([r.choice(M, 24, replace=False), [0, 127, 128, M - 1]]))
     cols = np.unique(np.concatenate([r.choice(N, 160, replace=False), [0, 31, 127, 128, 1023, 1024, N - 1]]))
     _check(Y, lay, X, b_max, rows, cols)
+
+
+# ------------------------------------------------ unpack once, then a dense GEMM
+
+def _from_fragments(buf, K, N):
+    """fp16 [K][N] from the B-fragment order ((k / 8) N_pad + n) 8 + k % 8."""
+    Np = -(-N // 128) * 128
+    kb = -(-K // 64) * 8
+    f = buf.view(np.float16).reshape(kb, Np, 8)
+    return f.transpose(0, 2, 1).reshape(kb * 8, Np)[:K, :N], f
+
+
+@pytest.mark.parametrize("K,N,cfg,mat,b_max", [(256, 256, 0, 0, 8), (300, 70, 5, 1, 8), (4097, 1056, 5, 3, 8),
+                                               (1000, 2080, 5, 4, 6), (17, 300, 5, 5, 4)])
+def test_unpack_dense_bit_exact(K, N, cfg, mat, b_max):
+    lay = layer(K, N, cfg, mat, b_max)
+    planes = grq.pack(_dev(lay.codes), b_max=b_max)
+    buf = grq.unpack_dense(planes, _dev(lay.scales), _dev(lay.zeros), K, N, b_max=b_max).cpu().numpy()
+    W, f = _from_fragments(buf, K, N)
+    want = oracle.dequant_dense_fp16(lay.codes, lay.scales, lay.zeros, b_max)
+    assert np.array_equal(W.view(np.uint16), want.view(np.uint16))
+    Np = -(-N // 128) * 128
+    full = f.transpose(0, 2, 1).reshape(-1, Np)
+    assert not full[K:].any() and not full[:, N:].any()      # padding is zero
+
+
+@pytest.mark.parametrize("M,K,N,cfg,mat,b_max", CASES)
+def test_unpacked_prefill_parity(M, K, N, cfg, mat, b_max):
+    lay = layer(K, N, cfg, mat, b_max)
+    X = _tokens(K, M, cfg, mat)
+    planes = grq.pack(_dev(lay.codes), b_max=b_max)
+    dense = grq.unpack_dense(planes, _dev(lay.scales), _dev(lay.zeros), K, N, b_max=b_max)
+    Y = grq.dense_gemm(_dev(X), dense, K, N)
+    torch.cuda.synchronize()
+    _check(Y.cpu().numpy(), lay, X, b_max)
+
+
+def test_unpacked_prefill_full_size_sampled():
+    M, K, N = 2048, 4096, 14336
+    lay = layer(K, N, 2, 4, 8)
+    X = _tokens(K, M, 2, 4)
+    planes = grq.pack(_dev(lay.codes))
+    dense = grq.unpack_dense(planes, _dev(lay.scales), _dev(lay.zeros), K, N)
+    Y = grq.dense_gemm(_dev(X), dense, K, N)
+    torch.cuda.synchronize()
+    Y = Y.cpu().numpy()
+    r = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([r.choice(M, 24, replace=False), [0, 255, 256, M - 1]]))
+    cols = np.unique(np.concatenate([r.choice(N, 160, replace=False), [0, 255, 256, 1023, 1024, N - 1]]))
+    _check(Y, lay, X, 8, rows, cols)

@@ -67,3 +67,19 @@ def test_prefill_group_indexing():
     Y = oracle.prefill(codes, scales, zeros, X)
     assert Y[0].tolist() == [1.0, 4.0, 12.0]
     assert Y[1].tolist() == [3.0, 2.25, 1.75]
+
+
+def test_dense_fp16_is_correctly_rounded():
+    """Every entry is the fp16 nearest to the exact s q + z (ties to even):
+    the two fp16 neighbours of the result bracket the exact value and the
+    result is the closer one."""
+    codes, scales, zeros, _ = _case(1, 300, 50, 21)
+    exact = oracle.dequant_dense(codes, scales, zeros)
+    r = oracle.dequant_dense_fp16(codes, scales, zeros)
+    up = np.nextafter(r, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(r, np.float16(-np.inf)).astype(np.float64)
+    rv = r.astype(np.float64)
+    assert np.all(np.abs(rv - exact) <= np.abs(up - exact))
+    assert np.all(np.abs(rv - exact) <= np.abs(dn - exact))
+    g = np.arange(300) // 128
+    assert np.array_equal(rv[5], (scales[g[5]].astype(np.float64) * codes[5] + zeros[g[5]].astype(np.float64)).astype(np.float16).astype(np.float64))
