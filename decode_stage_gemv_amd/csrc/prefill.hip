@@ -75,6 +75,7 @@ __device__ inline __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int64_t 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct PrefillArgs {
   const uint8_t* planes;
@@ -87,15 +88,22 @@ struct PrefillArgs {
 };
 
 // One step's global data for this thread (raw; see the buffer-load notes).
+// X chunks are 8 halves each: four dwords (VEC) or one half per register.
+template <bool VEC>
 struct StepRegs {
-  uint32_t x[kXChunks][4];   // X chunks: 8 halves each
+  uint32_t x[kXChunks][VEC ? 4 : 8];
   uint32_t w1[8], w2[8];     // plane words of the thread's two rows
   uint16_t s[2], z[2];       // scale and zero of the lane's two B-fragment columns
 };
 
 }  // namespace
 
-template <int BMAX>
+// VEC: K a multiple of 8 and X 16-byte aligned, so each 8-half X chunk is one
+// 16-byte load; otherwise eight 2-byte loads.  All global loads are
+// unconditional (past the end they read zero or repeat the last step), so
+// that the compiler's wait counts stay exact instead of draining every load
+// in flight at the loop head.
+template <int BMAX, bool VEC>
 __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kPM * kXPitch];
   __shared__ __attribute__((aligned(16))) uint32_t s_w[2][kFragRows * kPN * 4];
@@ -133,7 +141,6 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // (tid + 512 c) / 8, halves 8 ((tid + 512 c) % 8) .. + 7 of the step
   const int64_t mrows = (M - m0) < kPM ? (M - m0) : kPM;
   const __amdgpu_buffer_rsrc_t xrs = uniform_rsrc(a.X + m0 * K, mrows * K * 2);
-  const bool x_even = (K & 1) == 0;
   // B-fragment columns of this lane (one per column block cb)
   int ncol[2];
 #pragma unroll
@@ -142,27 +149,23 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     ncol[cb] = (int)(n < N ? n : N - 1);
   }
 
-  auto load_step = [&](int st, StepRegs& r) {
+  auto load_step = [&](int st, StepRegs<VEC>& r) {
     const int k0 = st * kPK;
 #pragma unroll
     for (int c = 0; c < kXChunks; ++c) {
       const int q = tid + c * kPThreads;
       const int k = k0 + 8 * (q & 7);
       const uint32_t rowb = (uint32_t)(q >> 3) * (uint32_t)K * 2u;
-      if (x_even) {
+      if constexpr (VEC) {
+        const uint32_t off = k < K ? rowb + (uint32_t)(2 * k) : kOOR;
+        const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)off, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t off = k + 2 * e < K ? rowb + (uint32_t)(2 * (k + 2 * e)) : kOOR;
-          r.x[c][e] = __builtin_amdgcn_raw_buffer_load_b32(xrs, (int)off, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e) r.x[c][e] = t[e];
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t o0 = k + 2 * e < K ? rowb + (uint32_t)(2 * (k + 2 * e)) : kOOR;
-          const uint32_t o1 = k + 2 * e + 1 < K ? rowb + (uint32_t)(2 * (k + 2 * e + 1)) : kOOR;
-          const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(xrs, (int)o0, 0, 0);
-          const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(xrs, (int)o1, 0, 0);
-          r.x[c][e] = lo | (hi << 16);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t off = k + e < K ? rowb + (uint32_t)(2 * (k + e)) : kOOR;
+          r.x[c][e] = __builtin_amdgcn_raw_buffer_load_b16(xrs, (int)off, 0, 0);
         }
       }
     }
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int kSh = 8 - BMAX;                              // codes come back as q 2^(8 - b_max)
   constexpr uint32_t kKeep = 0x01010101u * (0xFFu >> kSh);
   // rebuilt codes of one step (plane words in r) into B buffer dst
-  auto unpack = [&](const StepRegs& r, uint32_t* buf) {
+  auto unpack = [&](const StepRegs<VEC>& r, uint32_t* buf) {
     uint32_t d1[8], d2[8];
     planes_to_codes<BMAX>(r.w1, d1);
     planes_to_codes<BMAX>(r.w2, d2);
@@ -212,11 +215,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       }
     }
   };
-  auto write_x = [&](const uint32_t (&x)[kXChunks][4]) {
+  auto write_x = [&](const uint32_t (&x)[kXChunks][VEC ? 4 : 8]) {
 #pragma unroll
     for (int c = 0; c < kXChunks; ++c) {
       const int q = tid + c * kPThreads;
-      __builtin_memcpy(&s_x[(q >> 3) * kXPitch + 8 * (q & 7)], x[c], 16);
+      uint32_t d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (VEC) d[e] = x[c][e];
+        else d[e] = (x[c][2 * e] & 0xFFFFu) | (x[c][2 * e + 1] << 16);
+      }
+      __builtin_memcpy(&s_x[(q >> 3) * kXPitch + 8 * (q & 7)], d, 16);
     }
   };
 
@@ -267,8 +276,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
   // other buffer.  The two waves that share a SIMD (w and w + 4) do the two
   // halves in opposite order, so one's vector-ALU work overlaps the other's
   // matrix work.  X is single-buffered and rewritten between two barriers.
-  StepRegs r;
-  uint32_t s2[2], z2[2], xn[kXChunks][4];
+  StepRegs<VEC> r;
+  constexpr int kXRegs = VEC ? 4 : 8;
+  const int last = steps - 1;
+  uint32_t s2[2], z2[2], xn[kXChunks][kXRegs];
   load_step(0, r);
   unpack(r, s_w[0]);
   write_x(r.x);
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
     s2[cb] = (uint32_t)r.s[cb] * 0x00010001u;
     z2[cb] = (uint32_t)r.z[cb] * 0x00010001u;
   }
-  if (steps > 1) load_step(1, r);
+  load_step(last < 1 ? last : 1, r);
   __syncthreads();
   const bool matrix_first = wid >= kPWaves / 2;
   for (int st = 0; st < steps; ++st) {
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int c = 0; c < kXChunks; ++c)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xn[c][e] = r.x[c][e];
+        for (int e = 0; e < kXRegs; ++e) xn[c][e] = r.x[c][e];
     }
     uint32_t s2n[2], z2n[2];
 #pragma unroll
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       s2n[cb] = (uint32_t)r.s[cb] * 0x00010001u;
       z2n[cb] = (uint32_t)r.z[cb] * 0x00010001u;
     }
-    if (st + 2 < steps) load_step(st + 2, r);
+    load_step(st + 2 < last ? st + 2 : last, r);   // past the end: repeats the last step, unused
     if (!matrix_first) mfma_step(cur, s2, z2);
     __syncthreads();                 // MFMAs of st done with X; codes of st + 1 written
     if (more) write_x(xn);
@@ -336,15 +347,21 @@ int launch_prefill(const uint8_t* planes, const uint16_t* scales, const uint16_t
   if (mt * nh > 0x7FFFFFFF) return fail(GRINQH_EINVAL, "M x N needs more than 2^31 workgroups");
   PrefillArgs a{planes, scales, zeros, X, Y, M, K, N, (int)mt, (int)nh};
   const dim3 grid((unsigned)(mt * nh)), block(kPThreads);
-  switch (bmax) {
-    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL(prefill_kernel<3>, grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, block, 0, s, a); break;
-    case 5: hipLaunchKernelGGL(prefill_kernel<5>, grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL(prefill_kernel<6>, grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL(prefill_kernel<7>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(prefill_kernel<8>, grid, block, 0, s, a); break;
+  const bool vec = K % 8 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0;
+  switch (bmax * 2 + (vec ? 1 : 0)) {
+#define GRINQH_PREFILL_CASE(B)                                                        \
+  case 2 * B: hipLaunchKernelGGL((prefill_kernel<B, false>), grid, block, 0, s, a); break; \
+  case 2 * B + 1: hipLaunchKernelGGL((prefill_kernel<B, true>), grid, block, 0, s, a); break;
+    GRINQH_PREFILL_CASE(1)
+    GRINQH_PREFILL_CASE(2)
+    GRINQH_PREFILL_CASE(3)
+    GRINQH_PREFILL_CASE(4)
+    GRINQH_PREFILL_CASE(5)
+    GRINQH_PREFILL_CASE(6)
+    GRINQH_PREFILL_CASE(7)
+    GRINQH_PREFILL_CASE(8)
+#undef GRINQH_PREFILL_CASE
+    default: return fail(GRINQH_EINVAL, "b_max = %d outside 1..8", bmax);
   }
   return check_launch("grinqh_prefill");
 }
