@@ -166,14 +166,10 @@ class Prepared:
         self.ybufs = [torch.zeros(N, dtype=torch.float32, device=dev) for _ in range(2)]
         # algorithmic bytes of each copy's step, from the GPU's own assignment
         self.bytes, self.avg_bits = [], []
-        G = (K + 127) // 128
         for (_, _, _, x) in self.layer.copies:
-            bits, _, _ = grq.assign_bits(x, self.thresholds, self.levels)
-            b = bits.to(torch.int64)
-            pad = torch.zeros(G * 128 - K, dtype=torch.int64, device=dev)
-            active_groups = int((torch.cat([b, pad]).view(G, 128).amax(dim=1) > 0).sum().item())
-            self.bytes.append(int(b.sum().item()) * self.layer.np_cols // 8 + 4 * N * active_groups + 2 * K)
-            self.avg_bits.append(float(b.sum().item()) / K)
+            nb, avg = algorithmic_bytes(x, K, N, self.thresholds, self.levels, self.layer.np_cols)
+            self.bytes.append(nb)
+            self.avg_bits.append(avg)
         torch.cuda.synchronize()
         log(f"prepared {name} ({ENTRY[mode]}): avg bits {np.mean(self.avg_bits):.3f}, "
             f"{np.mean(self.bytes) / 1e6:.2f} MB/step")
@@ -230,6 +226,120 @@ class Prepared:
             ms = start.elapsed_time(stop) / steps
         step_bytes = float(np.mean([self.bytes[k % self.R] for k in range(steps)]))
         return ms, step_bytes
+
+
+def algorithmic_bytes(x, K, N, thresholds, levels, np_cols):
+    """Bytes one VMM must read for activation x: the planes of the widths the
+    GPU's own assignment gives, a scale and a zero per column of every group
+    with an active row, and x.  Also returns the average width."""
+    import torch
+    import decode_stage_gemv_amd as grq
+    bits, _, _ = grq.assign_bits(x, thresholds, levels)
+    b = bits.to(torch.int64)
+    G = (K + 127) // 128
+    pad = torch.zeros(G * 128 - K, dtype=torch.int64, device=b.device)
+    active_groups = int((torch.cat([b, pad]).view(G, 128).amax(dim=1) > 0).sum().item())
+    total = int(b.sum().item())
+    return total * np_cols // 8 + 4 * N * active_groups + 2 * K, total / K
+
+
+class Stack:
+    """One token's pass through the 36-layer Qwen3-8B linear stack: 252
+    matrices (q, k, v, o, gate, up, down per layer) packed at 8 bits and
+    resident together (6.95 GB of planes), each with its own activation and
+    thresholds calibrated for an average of 3 bits over levels {0,2,3,4,8}.
+
+    keep_cols > 0 keeps, per matrix, that many seeded columns (plus the first
+    and last) of the codes, scales and zeros on the host for parity checks."""
+
+    def __init__(self, keep_cols=0, progress=True):
+        import torch
+        import synthetic
+        import decode_stage_gemv_amd as grq
+        t0 = time.time()
+        dev = torch.device("cuda:0")
+        self.P, self.levels = synthetic.P_LEVELS_5[3], synthetic.LEVELS_5
+        self.mats = []
+        for idx, layer, name, K, N in synthetic.qwen3_stack():
+            codes, scales, zeros = synthetic.device_weights(K, N, synthetic.STACK_CONFIG, idx, dev)
+            planes = grq.pack(codes)
+            m = {"idx": idx, "layer": layer, "name": name, "K": K, "N": N,
+                 "planes": planes, "scales": scales, "zeros": zeros}
+            if keep_cols:
+                r = np.random.default_rng([synthetic.STACK_CONFIG, idx, 9])
+                cols = np.unique(np.concatenate([r.choice(N, keep_cols, replace=False), [0, N - 1]]))
+                ct = torch.from_numpy(cols).to(dev)
+                m["cols"] = cols
+                m["host"] = tuple(t.index_select(1, ct).cpu().numpy() for t in (codes, scales, zeros))
+            del codes
+            calib = torch.from_numpy(synthetic.make_calibration(K, synthetic.STACK_CONFIG, idx)).to(dev)
+            m["thresholds"] = [float(v) for v in grq.calibrate(calib, self.P).cpu().numpy()]
+            m["x_host"] = synthetic.make_activations(K, 1, synthetic.STACK_CONFIG, idx)[0]
+            m["x"] = torch.from_numpy(m["x_host"]).to(dev)
+            self.mats.append(m)
+            if progress and idx % 35 == 34:
+                log(f"stack: {idx + 1} of 252 matrices packed ({time.time() - t0:.1f}s)")
+        self.ys = [[torch.zeros(m["N"], dtype=torch.float32, device=dev) for m in self.mats] for _ in range(2)]
+        self.plane_bytes = sum(m["planes"].numel() for m in self.mats)
+        torch.cuda.synchronize()
+        log(f"stack: 252 matrices, {self.plane_bytes / 1e9:.2f} GB of planes resident, setup {time.time() - t0:.1f}s")
+
+    def token(self, t):
+        """One token's 252 VMMs (decode-loop form: add into output set t % 2,
+        clear set (t + 1) % 2 for the next token)."""
+        import decode_stage_gemv_amd as grq
+        ya, yb = self.ys[t % 2], self.ys[(t + 1) % 2]
+        for j, m in enumerate(self.mats):
+            grq.decode_vmm_accumulate(m["planes"], m["scales"], m["zeros"], m["x"], m["K"], m["N"],
+                                      m["thresholds"], self.levels, ya[j], yb[j])
+
+    def bytes_per_token(self):
+        import decode_stage_gemv_amd as grq
+        total, bits = 0, 0.0
+        for m in self.mats:
+            np_cols = int(grq.lib().grinqh_planes_bytes(1, m["N"], 8))
+            b, avg = algorithmic_bytes(m["x"], m["K"], m["N"], m["thresholds"], self.levels, np_cols)
+            total += b
+            bits += avg * m["K"] * m["N"]
+        return total, bits / sum(m["K"] * m["N"] for m in self.mats)
+
+
+def stack_bench(tokens=4, warmup=2):
+    """Time per token of the Qwen3-8B stack: `tokens` passes (252 launches
+    each) captured in one HIP graph, timed over one replay with events on the
+    capture stream."""
+    import torch
+    st = Stack()
+    nbytes, avg_bits = st.bytes_per_token()
+    for t in range(warmup):
+        st.token(t)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for t in range(tokens):
+                st.token(t)
+        g.replay()
+        s.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(s)
+        g.replay()
+        stop.record(s)
+        s.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / tokens
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out = {"model": "qwen3-8b linear stack (36 layers x q,k,v,o,gate,up,down)", "vmms_per_token": len(st.mats),
+           "entry_point": ENTRY["accumulate"], "avg_bits": avg_bits, "plane_bytes_resident": st.plane_bytes,
+           "bytes_per_token": nbytes, "us_per_token": us, "us_per_vmm": us / len(st.mats), "GB_s": gbs,
+           "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "tokens_timed": tokens}
+    log(f"stack: {us:.1f} us per token ({us / len(st.mats):.2f} us per VMM), {nbytes / 1e9:.3f} GB per token, "
+        f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak), avg bits {avg_bits:.3f}")
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
@@ -448,6 +558,9 @@ def main():
     ap.add_argument("--no-lut", action="store_true",
                     help="skip the table-reconstruction leg (grinqh_decode_vmm_lut)")
     ap.add_argument("--lut-only", action="store_true", help="time only grinqh_decode_vmm_lut")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the Qwen3-8B stack leg (252 VMMs per token, 6.95 GB of planes)")
+    ap.add_argument("--stack-only", action="store_true", help="time only the Qwen3-8B stack")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode VMM path runs on a single GPU "
@@ -460,6 +573,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.stack_only:
+        print(json.dumps({"stack": stack_bench()}), flush=True)
         return
     if args.lut_only:
         print(json.dumps({"lut": lut_bench(args.workload, min(args.steps, 100), min(args.warmup, 10))}), flush=True)
@@ -520,6 +636,10 @@ def main():
     if not args.no_lut and not args.only:
         lut = lut_bench(args.workload, min(args.steps, 100), min(args.warmup, 10))
 
+    stack = None
+    if not args.no_stack and not args.only:
+        stack = stack_bench()
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(prep)
     traffic = measured_traffic(args.workload, args.mode)
     out = {
@@ -555,6 +675,8 @@ def main():
         out["prefill"] = prefill
     if lut:
         out["lut"] = lut
+    if stack:
+        out["stack"] = stack
     print(json.dumps(out), flush=True)
 
 

@@ -28,6 +28,12 @@ only the model shapes):
 * Seeds: ``numpy.random.SeedSequence([config, matrix, role])`` with role 0 for
   W, 1 for the outlier channel set, 2 for calibration vectors, 3 for test
   vectors.
+* The 36-layer Qwen3-8B stack (252 matrices, 6.95 G weights) is too large to
+  draw on the host in reasonable time, so :func:`device_weights` draws its
+  weights on the GPU: the same N(0, 0.02^2) distribution from torch's
+  Philox generator seeded by the same (config, matrix, 0) triple, and the
+  same rounding rule evaluated in fp32.  Its activations and calibration
+  vectors are the NumPy ones above.
 """
 from __future__ import annotations
 
@@ -83,6 +89,7 @@ QWEN3_8B_LAYER = {
     "gate": (4096, 12288), "up": (4096, 12288), "down": (12288, 4096),
 }
 QWEN3_8B_LAYERS = 36
+STACK_CONFIG = 3     # config index of the Qwen3-8B stack
 LLAMA3_70B_MLP = {"gate": (8192, 28672), "down": (28672, 8192)}
 
 
@@ -244,3 +251,55 @@ def make_layer(K: int, N: int, config: int = 0, matrix: int = 0, n_test: int = 1
     calib = make_calibration(K, config, matrix, n_calib)
     x = make_activations(K, n_test, config, matrix, ROLE_TEST)
     return Layer(K, N, codes, scales, zeros, calib, x)
+
+
+def qwen3_stack():
+    """The 252 matrices one token passes through, in order: a list of
+    (matrix index, layer, name, K, N) with matrix index = 7 layer + position."""
+    out = []
+    for layer in range(QWEN3_8B_LAYERS):
+        for j, (name, (K, N)) in enumerate(QWEN3_8B_LAYER.items()):
+            out.append((len(QWEN3_8B_LAYER) * layer + j, layer, name, K, N))
+    return out
+
+
+def device_weights(K: int, N: int, config: int, matrix: int, device, b_max: int = 8):
+    """Seeded ``W ~ N(0, 0.02^2)`` drawn on a torch device and quantised there.
+
+    The rounding rule is :func:`rtn_quantize`'s (fp16 s = (max - min) / L and
+    z = min per group and column, q = clip(rint((w - z) / s), 0, L)), evaluated
+    in fp32.  Returns torch tensors (codes u8 [K][N], scales f16 [G][N],
+    zeros f16 [G][N]) on ``device``.
+    """
+    import torch
+    if not 1 <= b_max <= 8:
+        raise ValueError(f"b_max = {b_max}, expected 1..8")
+    seed = int(np.random.SeedSequence([config, matrix, ROLE_W]).generate_state(1, np.uint64)[0]) & ((1 << 63) - 1)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    w = torch.randn((K, N), generator=gen, device=device, dtype=torch.float32).mul_(WEIGHT_STD)
+    return rtn_quantize_torch(w, b_max)
+
+
+def rtn_quantize_torch(w, b_max: int = 8):
+    """:func:`rtn_quantize` on a torch fp32 tensor ``w[K][N]``, in fp32 on its device."""
+    import torch
+    top = float((1 << b_max) - 1)
+    K, N = w.shape
+    G = n_groups(K)
+    codes = torch.empty((K, N), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((G, N), dtype=torch.float16, device=w.device)
+    zeros = torch.empty((G, N), dtype=torch.float16, device=w.device)
+    for g in range(G):
+        blk = w[g * GROUP:(g + 1) * GROUP]
+        lo = blk.amin(dim=0)
+        hi = blk.amax(dim=0)
+        s16 = ((hi - lo) / top).to(torch.float16)
+        z16 = lo.to(torch.float16)
+        s32, z32 = s16.float(), z16.float()
+        q = torch.round((blk - z32) / s32)
+        q = torch.where(s32 == 0.0, torch.zeros_like(q), q)
+        codes[g * GROUP:(g + 1) * GROUP] = q.clamp_(0.0, top).to(torch.uint8)
+        scales[g] = s16
+        zeros[g] = z16
+    return codes, scales, zeros

@@ -74,3 +74,40 @@ def test_precision_tables(table, levels):
     for avg, P in table.items():
         assert sum(P) == pytest.approx(1.0, abs=1e-12)
         assert sum(p * b for p, b in zip(P, levels)) == pytest.approx(avg, abs=1e-12)
+
+
+def test_torch_rtn_matches_numpy_rule():
+    """The device quantiser applies rtn_quantize's rule (evaluated in fp32
+    instead of fp64): identical scales and zeros, and codes identical except
+    where w sits within fp32 rounding of a decision boundary."""
+    torch = pytest.importorskip("torch")
+    w = (np.random.default_rng(5).standard_normal((300, 70)) * 0.02).astype(np.float32)
+    for b_max in (8, 4):
+        c, s, z = synthetic.rtn_quantize(w, b_max)
+        ct, st, zt = (t.numpy() for t in synthetic.rtn_quantize_torch(torch.from_numpy(w), b_max))
+        assert np.array_equal(st.view(np.uint16), s.view(np.uint16))
+        assert np.array_equal(zt.view(np.uint16), z.view(np.uint16))
+        diff = ct.astype(np.int16) - c.astype(np.int16)
+        assert np.abs(diff).max() <= 1 and np.count_nonzero(diff) <= 2
+
+
+def test_device_weights_seeded_and_distributed():
+    torch = pytest.importorskip("torch")
+    a = synthetic.device_weights(256, 128, 3, 4, "cpu")
+    b = synthetic.device_weights(256, 128, 3, 4, "cpu")
+    c = synthetic.device_weights(256, 128, 3, 5, "cpu")
+    assert all(torch.equal(u, v) for u, v in zip(a, b))
+    assert not torch.equal(a[0], c[0])
+    codes, scales, zeros = a
+    g = torch.arange(256) // 128
+    w = codes.double() * scales.double()[g] + zeros.double()[g]
+    assert abs(w.std().item() - 0.02) < 0.001 and abs(w.mean().item()) < 0.001
+    assert codes.min().item() == 0 and codes.max().item() == 255     # every column spans its range
+
+
+def test_qwen3_stack_listing():
+    st = synthetic.qwen3_stack()
+    assert len(st) == 252
+    assert [m[0] for m in st] == list(range(252))
+    assert sum(K * N for _, _, _, K, N in st) == 36 * (2 * 4096 * 4096 + 2 * 4096 * 1024 + 3 * 4096 * 12288)
+    assert st[6] == (6, 0, "down", 12288, 4096) and st[-1][1] == 35
