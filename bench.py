@@ -246,46 +246,69 @@ def algorithmic_bytes(x, K, N, thresholds, levels, np_cols):
 class Stack:
     """One token's pass through the 36-layer Qwen3-8B linear stack: 252
     matrices (q, k, v, o, gate, up, down per layer) packed at 8 bits and
-    resident together (6.95 GB of planes), each with its own activation and
-    thresholds calibrated for an average of 3 bits over levels {0,2,3,4,8}.
+    resident together (6.95 GB of planes), calibrated for an average of 3
+    bits over levels {0,2,3,4,8}.
 
-    keep_cols > 0 keeps, per matrix, that many seeded columns (plus the first
+    fused=False: one VMM per matrix, each with its own activation and
+    thresholds (252 launches per token).  fused=True: the matrices that read
+    the same input in the model are packed side by side by columns, q|k|v
+    and gate|up, and share one activation and one set of thresholds (the
+    thresholds depend only on the input's calibration vectors), so a layer
+    takes 4 VMMs (144 launches per token); the weights are the same draws.
+
+    keep_cols > 0 keeps, per VMM, that many seeded columns (plus the first
     and last) of the codes, scales and zeros on the host for parity checks."""
 
-    def __init__(self, keep_cols=0, progress=True):
+    GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+    def __init__(self, keep_cols=0, fused=False, progress=True):
         import torch
         import synthetic
         import decode_stage_gemv_amd as grq
         t0 = time.time()
         dev = torch.device("cuda:0")
+        self.fused = fused
         self.P, self.levels = synthetic.P_LEVELS_5[3], synthetic.LEVELS_5
+        listing = synthetic.qwen3_stack()
+        if fused:
+            by = {(layer, name): (idx, K, N) for idx, layer, name, K, N in listing}
+            units = [[(by[(layer, n)][0], n) + by[(layer, n)][1:] for n in grp]
+                     for layer in range(synthetic.QWEN3_8B_LAYERS) for grp in self.GROUPS]
+        else:
+            units = [[(idx, name, K, N)] for idx, _, name, K, N in listing]
         self.mats = []
-        for idx, layer, name, K, N in synthetic.qwen3_stack():
-            codes, scales, zeros = synthetic.device_weights(K, N, synthetic.STACK_CONFIG, idx, dev)
+        for u, unit in enumerate(units):
+            idx0, K = unit[0][0], unit[0][2]
+            parts = [synthetic.device_weights(K, N, synthetic.STACK_CONFIG, idx, dev) for idx, _, _, N in unit]
+            codes, scales, zeros = (torch.cat([p[i] for p in parts], dim=1) if len(parts) > 1 else parts[0][i]
+                                    for i in range(3))
+            del parts
+            N = codes.shape[1]
             planes = grq.pack(codes)
-            m = {"idx": idx, "layer": layer, "name": name, "K": K, "N": N,
+            m = {"idx": idx0, "name": "|".join(n for _, n, _, _ in unit), "K": K, "N": N,
                  "planes": planes, "scales": scales, "zeros": zeros}
             if keep_cols:
-                r = np.random.default_rng([synthetic.STACK_CONFIG, idx, 9])
+                r = np.random.default_rng([synthetic.STACK_CONFIG, idx0, 9 + len(unit)])
                 cols = np.unique(np.concatenate([r.choice(N, keep_cols, replace=False), [0, N - 1]]))
                 ct = torch.from_numpy(cols).to(dev)
                 m["cols"] = cols
                 m["host"] = tuple(t.index_select(1, ct).cpu().numpy() for t in (codes, scales, zeros))
             del codes
-            calib = torch.from_numpy(synthetic.make_calibration(K, synthetic.STACK_CONFIG, idx)).to(dev)
+            calib = torch.from_numpy(synthetic.make_calibration(K, synthetic.STACK_CONFIG, idx0)).to(dev)
             m["thresholds"] = [float(v) for v in grq.calibrate(calib, self.P).cpu().numpy()]
-            m["x_host"] = synthetic.make_activations(K, 1, synthetic.STACK_CONFIG, idx)[0]
+            m["x_host"] = synthetic.make_activations(K, 1, synthetic.STACK_CONFIG, idx0)[0]
             m["x"] = torch.from_numpy(m["x_host"]).to(dev)
             self.mats.append(m)
-            if progress and idx % 35 == 34:
-                log(f"stack: {idx + 1} of 252 matrices packed ({time.time() - t0:.1f}s)")
+            if progress and u % 36 == 35:
+                log(f"stack: {u + 1} of {len(units)} VMMs packed ({time.time() - t0:.1f}s)")
         self.ys = [[torch.zeros(m["N"], dtype=torch.float32, device=dev) for m in self.mats] for _ in range(2)]
         self.plane_bytes = sum(m["planes"].numel() for m in self.mats)
         torch.cuda.synchronize()
-        log(f"stack: 252 matrices, {self.plane_bytes / 1e9:.2f} GB of planes resident, setup {time.time() - t0:.1f}s")
+        log(f"stack{' (fused projections)' if fused else ''}: {len(self.mats)} VMMs per token, "
+            f"{self.plane_bytes / 1e9:.2f} GB of planes resident, setup {time.time() - t0:.1f}s")
 
     def token(self, t):
-        """One token's 252 VMMs (decode-loop form: add into output set t % 2,
+        """One token's VMMs (decode-loop form: add into output set t % 2,
         clear set (t + 1) % 2 for the next token)."""
         import decode_stage_gemv_amd as grq
         ya, yb = self.ys[t % 2], self.ys[(t + 1) % 2]
@@ -304,12 +327,11 @@ class Stack:
         return total, bits / sum(m["K"] * m["N"] for m in self.mats)
 
 
-def stack_bench(tokens=4, warmup=2):
-    """Time per token of the Qwen3-8B stack: `tokens` passes (252 launches
-    each) captured in one HIP graph, timed over one replay with events on the
-    capture stream."""
+def stack_bench(fused=False, tokens=4, warmup=2):
+    """Time per token of the Qwen3-8B stack: `tokens` passes captured in one
+    HIP graph, timed over one replay with events on the capture stream."""
     import torch
-    st = Stack()
+    st = Stack(fused=fused)
     nbytes, avg_bits = st.bytes_per_token()
     for t in range(warmup):
         st.token(t)
@@ -331,13 +353,17 @@ def stack_bench(tokens=4, warmup=2):
         s.synchronize()
     us = start.elapsed_time(stop) * 1e3 / tokens
     gbs = nbytes / (us * 1e-6) / 1e9
-    out = {"model": "qwen3-8b linear stack (36 layers x q,k,v,o,gate,up,down)", "vmms_per_token": len(st.mats),
-           "entry_point": ENTRY["accumulate"], "avg_bits": avg_bits, "plane_bytes_resident": st.plane_bytes,
-           "bytes_per_token": nbytes, "us_per_token": us, "us_per_vmm": us / len(st.mats), "GB_s": gbs,
-           "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "tokens_timed": tokens}
-    log(f"stack: {us:.1f} us per token ({us / len(st.mats):.2f} us per VMM), {nbytes / 1e9:.3f} GB per token, "
-        f"{gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak), avg bits {avg_bits:.3f}")
-    del st
+    n = len(st.mats)
+    out = {"model": "qwen3-8b linear stack (36 layers x q,k,v,o,gate,up,down)",
+           "form": ("fused projections: q|k|v and gate|up packed side by side, sharing x and thresholds"
+                    if fused else "one VMM per matrix, fresh x per VMM"),
+           "vmms_per_token": n, "entry_point": ENTRY["accumulate"], "avg_bits": avg_bits,
+           "plane_bytes_resident": st.plane_bytes, "bytes_per_token": nbytes, "us_per_token": us,
+           "us_per_vmm": us / n, "GB_s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "tokens_timed": tokens}
+    log(f"stack{' fused' if fused else ''}: {us:.1f} us per token ({us / n:.2f} us per VMM, {n} VMMs), "
+        f"{nbytes / 1e9:.3f} GB per token, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak), "
+        f"avg bits {avg_bits:.3f}")
+    del st, g
     torch.cuda.empty_cache()
     return out
 
@@ -575,7 +601,7 @@ def main():
         copy_probe()
         return
     if args.stack_only:
-        print(json.dumps({"stack": stack_bench()}), flush=True)
+        print(json.dumps({"stack": stack_bench(), "stack_fused": stack_bench(fused=True)}), flush=True)
         return
     if args.lut_only:
         print(json.dumps({"lut": lut_bench(args.workload, min(args.steps, 100), min(args.warmup, 10))}), flush=True)
@@ -636,9 +662,10 @@ def main():
     if not args.no_lut and not args.only:
         lut = lut_bench(args.workload, min(args.steps, 100), min(args.warmup, 10))
 
-    stack = None
+    stack = stack_fused = None
     if not args.no_stack and not args.only:
         stack = stack_bench()
+        stack_fused = stack_bench(fused=True)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(prep)
     traffic = measured_traffic(args.workload, args.mode)
@@ -677,6 +704,7 @@ def main():
         out["lut"] = lut
     if stack:
         out["stack"] = stack
+        out["stack_fused"] = stack_fused
     print(json.dumps(out), flush=True)
 
 

@@ -1,6 +1,7 @@
-"""One token through the 36-layer Qwen3-8B linear stack (252 VMMs, the whole
-8-plane store resident), in the launch configuration the stack benchmark
-times, checked on sampled columns of every matrix against the fp64 oracle.
+"""One token through the 36-layer Qwen3-8B linear stack (252 VMMs, or 144
+with q|k|v and gate|up packed side by side; the whole 8-plane store
+resident), in the launch configuration the stack benchmark times, checked on
+sampled columns of every VMM against the fp64 oracle.
 
 Per matrix: the GPU's calibrated thresholds must equal the oracle's bit for
 bit, and every sampled output must satisfy
@@ -23,10 +24,12 @@ REL_TOL = 1e-3
 ABS_TOL = 1e-4
 
 
-def test_qwen3_stack_one_token_sampled_columns():
+@pytest.mark.parametrize("fused", [False, True], ids=["per-matrix", "fused-projections"])
+def test_qwen3_stack_one_token_sampled_columns(fused):
     import bench
-    print("building the Qwen3-8B stack", file=sys.stderr, flush=True)
-    st = bench.Stack(keep_cols=6)
+    print(f"building the Qwen3-8B stack (fused={fused})", file=sys.stderr, flush=True)
+    st = bench.Stack(keep_cols=6, fused=fused)
+    assert len(st.mats) == (144 if fused else 252)
     st.token(0)                      # adds into output set 0 (zero), clears set 1
     torch.cuda.synchronize()
     bad = []
@@ -46,3 +49,5 @@ def test_qwen3_stack_one_token_sampled_columns():
             bad.append((m["idx"], m["name"], float(err.max())))
         assert not torch.any(st.ys[1][j]).item(), f"output set 1 of matrix {m['idx']} not cleared"
     assert not bad, f"matrices out of tolerance: {bad[:5]}"
+    del st
+    torch.cuda.empty_cache()
