@@ -523,8 +523,10 @@ def copy_probe(nbytes=512 << 20, reps=20):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / reps
     gbs = 2 * nbytes / (ms * 1e-3) / 1e9
-    print(json.dumps({"copy_probe": {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms,
-                                     "GB_s_read_plus_write": gbs}}), flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "GB_s_read_plus_write": gbs,
+            "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
 def cpu_baseline(prep, budget_s=15.0):
@@ -604,7 +606,7 @@ def main():
         sys.exit(2)
 
     if args.copy_probe:
-        copy_probe()
+        print(json.dumps({"copy_probe": copy_probe()}), flush=True)
         return
     if args.stack_only:
         print(json.dumps({"stack": stack_bench(), "stack_fused": stack_bench(fused=True)}), flush=True)
@@ -660,6 +662,11 @@ def main():
         if len(fit_pts) >= 3:
             sweep["linear_fit_70b_gate"] = linear_fit(fit_pts)
             log(f"70B gate linear fit: {sweep['linear_fit_70b_gate']}")
+        all_pts = [(v["bytes"], v["us_per_vmm"]) for k, v in sweep.items() if k in SWEEP]
+        if len(all_pts) >= 3:
+            # one line over every shape of the sweep (4096^2, 4096x14336, 70B gate)
+            sweep["linear_fit_all_shapes"] = linear_fit(all_pts)
+            log(f"linear fit over all swept shapes: {sweep['linear_fit_all_shapes']}")
 
     prefill = None
     if args.prefill_tokens > 0 and not args.only:
@@ -673,6 +680,9 @@ def main():
         stack = stack_bench()
         stack_fused = stack_bench(fused=True)
 
+    copy = copy_probe()
+    log(f"copy probe: {copy['GB_s_read_plus_write']:.0f} GB/s read + write "
+        f"({copy['frac_of_hbm_peak']:.1%} of the 8 TB/s peak); the VMM reaches {gbs / copy['GB_s_read_plus_write']:.1%} of it")
     cpu = None if args.no_cpu_baseline else cpu_baseline(prep)
     traffic = measured_traffic(args.workload, args.mode)
     out = {
@@ -700,6 +710,7 @@ def main():
                      "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": cpu,
     }
+    out["copy_probe"] = dict(copy, vmm_frac_of_copy=gbs / copy["GB_s_read_plus_write"])
     if others:
         out["other_entry_points"] = others
     if sweep:
