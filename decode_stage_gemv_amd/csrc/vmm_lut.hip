@@ -38,6 +38,8 @@ constexpr int kLThreads = 64 * kLWaves;
 constexpr int kLRowsPerPass = kLThreads / kLWords;   // rows processed per pass (128)
 constexpr int kLMaxRows = 2048;             // rows per workgroup
 constexpr int kLTargetWGs = 512;            // two resident workgroups per CU
+constexpr int kLSlices = kTile / kLCols;    // 128-column slices per store tile (8)
+constexpr int kLXCDs = 8;                   // MI355X
 
 struct LutArgs {
   const uint8_t* planes;
@@ -47,6 +49,7 @@ struct LutArgs {
   float* clear;
   int64_t K, N;
   int bmax, rows, n_ct;
+  int splits;              // row splits
   int lut_halves;          // LDS halves taken by the tables (at least the reduction buffer)
   int toff[9];             // LDS offset (halves) of width b's table; -1 if not in use
   int nused;               // widths in use
@@ -55,12 +58,31 @@ struct LutArgs {
 };
 
 constexpr int kLRedFloats = kLWaves * kLCols;   // wave reduction buffer, aliased on the tables
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+constexpr uint32_t kLOutOfRange = 0x7FFFFF00u;  // buffer offset past every range used here
+constexpr int kLRsrcWord3 = 0x00020000;         // raw 32-bit buffer, gfx9 family
+
+// Raw buffer descriptor from values that are the same in every lane (the
+// read-first-lane keeps the compiler from treating it as divergent).
+__device__ inline __amdgpu_buffer_rsrc_t lut_rsrc(const void* base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           kLRsrcWord3);
+}
 
 }  // namespace
 
 // LDS: tables, then x (fp16) and the list of active rows (u16 offsets) and
 // widths (u8) of the workgroup's rows, and a counter.
-int lut_smem_bytes(const LutArgs& a) { return a.lut_halves * 2 + a.rows * 2 + a.rows * 2 + a.rows + 16; }
+// The row list holds each width's rows in a run padded to a multiple of 32
+// entries (at most 31 padding entries for each of the 8 widths).
+constexpr int kLListPad = 8 * 32;
+int lut_smem_bytes(const LutArgs& a) {
+  return a.lut_halves * 2 + a.rows * 2 + (a.rows + kLListPad) * 2 + a.rows + 16;
+}
 
 // LDS position (halves) of entry p of column c in a width-b table block.
 __device__ inline int lut_at(int c, int p, int stride) { return c * stride + 16 * (c >> 5) + p; }
@@ -72,17 +94,27 @@ void vmm_lut_kernel(LutArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
   uint16_t* s_lut = s_dyn;
   uint16_t* s_xv = s_dyn + a.lut_halves;
-  uint16_t* s_act = s_xv + a.rows;                            // active rows, in no particular order
-  uint8_t* s_b = reinterpret_cast<uint8_t*>(s_act + a.rows);
-  __shared__ int s_nact;
+  uint16_t* s_act = s_xv + a.rows;                            // active rows by width (see below)
+  uint8_t* s_b = reinterpret_cast<uint8_t*>(s_act + a.rows + kLListPad);
+  __shared__ int s_cnt[9], s_cur[9], s_ub[10];
   float* s_red = reinterpret_cast<float*>(s_dyn);   // after the row loop the tables are dead
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t K = a.K, N = a.N;
-  const int cti = blockIdx.x % a.n_ct;
-  const int split = blockIdx.x / a.n_ct;
+  // workgroup -> (store tile, row split, 128-column slice), slices fastest,
+  // then splits: the eight slices of a store tile read the same 128-byte
+  // plane lines (16 bytes each) and the splits of a tile the same tables, so
+  // consecutive entries of this order are placed on one XCD (hardware
+  // workgroup ids go round-robin over the 8 XCDs) and share its L2
+  int L = blockIdx.x;
+  const int T = gridDim.x;
+  if (T % kLXCDs == 0) L = (L % kLXCDs) * (T / kLXCDs) + L / kLXCDs;
+  const int sub = L % kLSlices;
+  const int split = (L / kLSlices) % a.splits;
+  const int cti = (L / kLSlices / a.splits) * kLSlices + sub;
+  if (cti >= a.n_ct) return;       // a slice past a narrow last tile
   const int64_t n0 = (int64_t)cti * kLCols;
   const int64_t k0 = (int64_t)split * a.rows;
   const int nrows = (int)((K - k0) < a.rows ? (K - k0) : a.rows);
@@ -97,7 +129,10 @@ void vmm_lut_kernel(LutArgs a) {
   // 128 columns' tables of width b are one contiguous run in global memory,
   // copied with loads of up to 16 bytes, all loads of a round issued before
   // its stores.
-  if (tid == 0) s_nact = 0;
+  if (tid < 9) {
+    s_cnt[tid] = 0;
+    s_cur[tid] = 0;
+  }
   {
     const int cols = (int)((N - n0) < kLCols ? (N - n0) : kLCols);      // columns that exist
     for (int u = 0; u < a.nused; ++u) {
@@ -140,72 +175,143 @@ void vmm_lut_kernel(LutArgs a) {
       else copy(std::integral_constant<int, 2>());
     }
   }
-  // ---- activations and widths of this workgroup's rows
+  // ---- activations and widths of this workgroup's rows; the active rows
+  // are listed by width: width b's rows fill entries 32 ub[b] .. of the list
+  // (in no particular order), padded with 0xFFFF up to 32 ub[b + 1], so that
+  // every run of 32 entries (a "unit") holds rows of one width
   const AssignRegs ar = load_assign_regs(a.ap);
-  __syncthreads();                 // s_nact cleared
+  __syncthreads();                 // counters cleared
   for (int r = tid; r < nrows; r += kLThreads) {
     const uint16_t xv = a.x[k0 + r];
     const uint32_t b = bits_of(xv, ar);
     s_xv[r] = xv;
     s_b[r] = (uint8_t)b;
-    if (b > 0) s_act[atomicAdd(&s_nact, 1)] = (uint16_t)r;
+    if (b > 0) atomicAdd(&s_cnt[b], 1);
   }
   __syncthreads();
-  const int nact = s_nact;
+  if (tid == 0) {
+    int u = 0;
+    for (int b = 1; b <= 8; ++b) {
+      s_ub[b] = u;
+      u += (s_cnt[b] + 31) >> 5;
+    }
+    s_ub[9] = u;
+  }
+  __syncthreads();
+  for (int r = tid; r < nrows; r += kLThreads) {
+    const int b = s_b[r];
+    if (b > 0) s_act[32 * s_ub[b] + atomicAdd(&s_cur[b], 1)] = (uint16_t)r;
+  }
+  if (tid < 8 * 32) {
+    const int b = 1 + (tid >> 5);
+    const int e = s_cnt[b] + (tid & 31);
+    if (e < 32 * (s_ub[b + 1] - s_ub[b])) s_act[32 * s_ub[b] + e] = 0xFFFFu;
+  }
+  __syncthreads();
+  int ub[10];                      // first unit of each width (wave-uniform)
+#pragma unroll
+  for (int b = 1; b <= 9; ++b) ub[b] = __builtin_amdgcn_readfirstlane(s_ub[b]);
+  const int units = ub[9];
 
-  // ---- rows: lane = (row slot rs, word wl); pass q covers rows q*128 .. +127
+  // ---- units: lane = (row pair ps, word wl); a wave takes units wid,
+  // wid + 8, ...; all 32 rows of a unit have one width, so the rebuild and
+  // the table strides are specialised for it
   const int wl = tid & (kLWords - 1);
-  const int rs = tid >> 2;
-  const int passes = (nact + kLRowsPerPass - 1) / kLRowsPerPass;
-  const uint8_t* wbase = a.planes + 4 * (word0 + wl);
+  const int ps = lane >> 2;        // row pair of the unit: entries 2 ps, 2 ps + 1
+  // buffer over this workgroup's row tiles: row r at r rstride, plane p at
+  // scalar offset p pb, this lane's word at 4 (word0 + wl)
+  const uint32_t rstride = (uint32_t)(pb * bmax);
+  const __amdgpu_buffer_rsrc_t prs =
+      lut_rsrc(a.planes + store_offset(t0 * K + k0 * ct, bmax), (int64_t)(nrows > 0 ? nrows : 1) * rstride);
+  const uint32_t woff = 4u * (uint32_t)(word0 + wl);
   float acc[32];
 #pragma unroll
   for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
 
-  // plane words of the lane's row in pass q (planes past its width are 0)
-  auto load_pass = [&](int q, uint32_t (&w)[8], int& b, uint16_t& xv) {
-    const int slot = q * kLRowsPerPass + rs;
-    const int r = slot < nact ? s_act[slot] : 0;
-    b = slot < nact ? s_b[r] : 0;
-    xv = slot < nact ? s_xv[r] : (uint16_t)0;
-    const uint8_t* base = wbase + store_offset(t0 * K + (k0 + r) * ct, bmax);
+  // plane words of the lane's two rows in unit u, the unit's width and the
+  // rows' activations as an fp16 pair.  Every load is issued: planes past
+  // the width, padding rows and units past the end use an out-of-range
+  // offset (reads 0, moves no bytes), so the loads need no branch and the
+  // next unit's loads stay in flight while one is processed.
+  struct Unit {
+    uint32_t w1[8], w2[8];
+    uint32_t xw;
+    int b;
+  };
+  auto load_unit = [&](int u, Unit& t) {
+    int b = 0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) w[p] = p < b ? *reinterpret_cast<const uint32_t*>(base + p * pb) : 0u;
+    for (int v = 1; v <= 8; ++v) b = (u >= ub[v] && u < ub[v + 1]) ? v : b;
+    t.b = b;
+    const int uu = u < units ? u : 0;
+    const uint32_t e1 = b > 0 ? s_act[32 * uu + 2 * ps] : 0xFFFFu;
+    const uint32_t e2 = b > 0 ? s_act[32 * uu + 2 * ps + 1] : 0xFFFFu;
+    const uint32_t x1 = e1 != 0xFFFFu ? s_xv[e1] : 0u;
+    const uint32_t x2 = e2 != 0xFFFFu ? s_xv[e2] : 0u;
+    t.xw = x1 | (x2 << 16);
+    const uint32_t v1 = e1 != 0xFFFFu ? e1 * rstride + woff : kLOutOfRange;
+    const uint32_t v2 = e2 != 0xFFFFu ? e2 * rstride + woff : kLOutOfRange;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      t.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)(p < b ? v1 : kLOutOfRange), p < bmax ? p * pb : 0, 0);
+      t.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)(p < b ? v2 : kLOutOfRange), p < bmax ? p * pb : 0, 0);
+    }
+  };
+  // one unit of width B: rebuild the two rows' codes, look both weights of
+  // each column up (table index = the code's top B bits), and add
+  // x1 w1 + x2 w2 with one fp16 dot into the column's fp32 accumulator
+  auto process = [&](const Unit& t, auto bw) {
+    constexpr int B = decltype(bw)::value;
+    constexpr int kStride = (1 << B) + 2;                // halves per column table in LDS
+    uint32_t d1[8], d2[8];
+    planes_to_codes<B>(t.w1, d1);                        // plane p at code bit 7 - p
+    planes_to_codes<B>(t.w2, d2);
+    const char* tb = reinterpret_cast<const char*>(s_lut + a.toff[B] + lut_at(32 * wl, 0, kStride));
+    const half2_t xh = __builtin_bit_cast(half2_t, t.xw);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 4 * m + j;                         // column within the word
+        // byte offset 2 p of table entry p: bits 7 - B .. 7 of the code byte
+        // (bit 7 - B is zero after the rebuild)
+        uint32_t o1, o2;
+        if constexpr (B < 8) {
+          o1 = __builtin_amdgcn_ubfe(d1[m], 8u * j + 7u - B, B + 1u);
+          o2 = __builtin_amdgcn_ubfe(d2[m], 8u * j + 7u - B, B + 1u);
+        } else {
+          o1 = __builtin_amdgcn_ubfe(d1[m], 8u * j, 8u) << 1;
+          o2 = __builtin_amdgcn_ubfe(d2[m], 8u * j, 8u) << 1;
+        }
+        const _Float16 lo = *reinterpret_cast<const _Float16*>(tb + 2 * c * kStride + o1);
+        const _Float16 hi = *reinterpret_cast<const _Float16*>(tb + 2 * c * kStride + o2);
+        acc[c] = __builtin_amdgcn_fdot2((half2_t){lo, hi}, xh, acc[c], false);
+      }
+    }
+  };
+  auto process_rt = [&](const Unit& t) {
+    switch (t.b) {
+      case 1: process(t, std::integral_constant<int, 1>()); break;
+      case 2: process(t, std::integral_constant<int, 2>()); break;
+      case 3: process(t, std::integral_constant<int, 3>()); break;
+      case 4: process(t, std::integral_constant<int, 4>()); break;
+      case 5: process(t, std::integral_constant<int, 5>()); break;
+      case 6: process(t, std::integral_constant<int, 6>()); break;
+      case 7: process(t, std::integral_constant<int, 7>()); break;
+      case 8: process(t, std::integral_constant<int, 8>()); break;
+      default: break;
+    }
   };
 
-  uint32_t wc[8];
-  int bc;
-  uint16_t xc;
-  if (passes > 0) load_pass(0, wc, bc, xc);
-  for (int q = 0; q < passes; ++q) {
-    uint32_t wn[8];
-    int bn = 0;
-    uint16_t xn = 0;
-    if (q + 1 < passes) load_pass(q + 1, wn, bn, xn);
-    if (bc > 0) {
-      uint32_t d[8];
-      planes_to_codes<8>(wc, d);   // plane p at code bit 7 - p: q 2^(8 - b_max) with low bits cleared
-      const uint32_t shift = 8u - (uint32_t)bc;          // prefix = top bc bits of each code byte
-      const uint32_t stride = (1u << bc) + 2u;           // halves per column table in LDS
-      const uint16_t* tab = s_lut + a.toff[bc] + lut_at(32 * wl, 0, (int)stride);
-      const float xf = half_bits_to_float(xc);
-      uint16_t wv[32];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = 4 * m + j;                       // column within the word
-          const uint32_t p = __builtin_amdgcn_ubfe(d[m], 8u * j + shift, (uint32_t)bc);
-          wv[c] = tab[(uint32_t)c * stride + p];
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 32; ++c) acc[c] = __builtin_fmaf(xf, half_bits_to_float(wv[c]), acc[c]);
-    }
-#pragma unroll
-    for (int p = 0; p < 8; ++p) wc[p] = wn[p];
-    bc = bn;
-    xc = xn;
+  // two register sets in turn (no copies between them: a register copy of
+  // a loaded value would wait for the load), the next unit always in flight
+  Unit tA, tB;
+  load_unit(wid, tA);
+  for (int u = wid; u < units; u += 2 * kLWaves) {
+    load_unit(u + kLWaves, tB);                          // past the end: nothing moves
+    process_rt(tA);
+    load_unit(u + 2 * kLWaves, tA);
+    process_rt(tB);
   }
 
   // ---- reduce: lanes sharing a word (lane bits 2..5), then the waves
@@ -267,8 +373,10 @@ int launch_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x
   rows = (rows + 7) / 8 * 8;
   splits = (K + rows - 1) / rows;
   a.rows = (int)rows;
-  if ((int64_t)a.n_ct * splits > 0x7FFFFFFF)
-    return fail(GRINQH_EINVAL, "%lld workgroups: more than one launch handles", (long long)(a.n_ct * splits));
+  a.splits = (int)splits;
+  const int64_t wgs = (a.n_ct + kLSlices - 1) / kLSlices * kLSlices * splits;
+  if (wgs > 0x7FFFFFFF)
+    return fail(GRINQH_EINVAL, "%lld workgroups: more than one launch handles", (long long)wgs);
   const int smem = lut_smem_bytes(a);
   static bool attr_set = false;
   if (!attr_set) {
@@ -277,7 +385,7 @@ int launch_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x
     if (e != hipSuccess) return fail(GRINQH_EDEVICE, "grinqh_decode_vmm_lut: %s", hipGetErrorString(e));
     attr_set = true;
   }
-  hipLaunchKernelGGL(vmm_lut_kernel, dim3((unsigned)(a.n_ct * splits)), dim3(kLThreads), smem, s, a);
+  hipLaunchKernelGGL(vmm_lut_kernel, dim3((unsigned)wgs), dim3(kLThreads), smem, s, a);
   return check_launch("grinqh_decode_vmm_lut");
 }
 
