@@ -13,13 +13,18 @@
 // for its columns into LDS (column c's 2^b entries at c (2^b + 2) + 16 (c / 32)
 // halves: a copy of contiguous runs, and the padding spreads the lanes'
 // random lookups over the banks), computes the rows' widths (assignment of
-// section 3.1, fused) and lists the rows of non-zero width (rows of width 0
-// are never touched again).  Then each lane takes one listed row and one
-// plane word (32 columns) at a time: it loads only the top b planes of that
-// row (section 3.3), rebuilds the 32 codes with the bit transpose of
-// bitplane.hpp, and for each column looks the weight up in LDS and adds
-// x_i * w into an fp32 accumulator for that column.  The next chunk's plane
-// words are in flight while a chunk is processed.  At the end the lanes that share a word are reduced with
+// section 3.1, fused) and lists the rows of non-zero width grouped by width,
+// each width's run padded to a multiple of 32 (rows of width 0 are never
+// touched again).  A run of 32 listed rows of one width is a "unit"; a wave
+// takes units in turn, lane (row pair, plane word) loading only the top b
+// planes of its two rows (section 3.3), rebuilding their codes with the bit
+// transpose of bitplane.hpp specialised for b, looking up both rows' weights
+// of each of its 32 columns in LDS (constant table strides for b) and adding
+// x1 w1 + x2 w2 with one fp16 dot into the column's fp32 accumulator.  The
+// next unit's plane words are in flight while a unit is processed.
+// Workgroups that share a store tile are numbered onto one XCD (its eight
+// 128-column slices read the same plane lines, its row splits the same
+// tables).  At the end the lanes that share a word are reduced with
 // shuffles, the waves in LDS, and the sums are added into y with fp32
 // atomics (so y accumulates, as the accumulating uniform entry point does).
 #include <type_traits>
@@ -344,6 +349,8 @@ void vmm_lut_kernel(LutArgs a) {
 
 int launch_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x, int64_t K, int64_t N,
                    int bmax, const AssignParams& ap, float* y, float* clear, hipStream_t s) {
+  if (reinterpret_cast<uintptr_t>(lut) % 4 != 0)
+    return fail(GRINQH_EINVAL, "grinqh_decode_vmm_lut: the table buffer must be 4-byte aligned");
   LutArgs a{};
   a.planes = planes; a.lut = lut; a.x = x; a.y = y; a.clear = clear;
   a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;

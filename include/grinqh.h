@@ -214,12 +214,13 @@ int64_t grinqh_lut_entries(int64_t N, int b_max);
  * read.  Sums are fp32, added into y with fp32 device-scope atomics (the
  * order of the additions is not fixed).
  * planes:  the store (layout above) of the b_max-bit parent codes.
- * lut:     fp16 [grinqh_lut_entries(N, b_max)], layout above.
+ * lut:     fp16 [grinqh_lut_entries(N, b_max)], layout above, 4-byte aligned.
  * x:       fp16 [K].  thresholds, levels, n: as in grinqh_assign_bits, levels
  *          at most b_max.
  * y:       fp32 [N], read and updated.  clear: fp32 [N] or NULL, set to zero
  *          by this call (it must not overlap y).
- * Errors: as grinqh_decode_vmm_accumulate, and EINVAL for a NULL table.
+ * Errors: as grinqh_decode_vmm_accumulate, and EINVAL for a NULL or
+ * misaligned table.
  */
 int grinqh_decode_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x, int64_t K, int64_t N,
                           int b_max, const float* thresholds, const uint8_t* levels, int n, float* y,

@@ -179,3 +179,21 @@ def test_unpacked_prefill_validation(lib):
     assert lib.grinqh_dense_gemm(FAKE, FAKE, 0, 64, 64, FAKE, None) == g.EINVAL
     assert lib.grinqh_dense_gemm(FAKE, FAKE, 4, 1 << 21, 64, FAKE, None) == g.EINVAL
     assert lib.grinqh_dense_gemm(None, FAKE, 4, 64, 64, FAKE, None) == g.EINVAL
+
+
+def test_lut_validation(lib):
+    assert lib.grinqh_lut_entries(14336, 8) == 14336 * 510
+    assert lib.grinqh_lut_entries(100, 4) == 100 * 30
+    assert lib.grinqh_lut_entries(0, 8) == -1 and lib.grinqh_lut_entries(64, 9) == -1
+    th = (ctypes.c_float * 1)(1.0)
+    lv = (ctypes.c_uint8 * 2)(0, 8)
+    thp, lvp = ctypes.cast(th, ctypes.c_void_p), ctypes.cast(lv, ctypes.c_void_p)
+    y = 0x100000
+    r = lib.grinqh_decode_vmm_lut(FAKE, None, FAKE, 128, 64, 8, thp, lvp, 1, y, None, None)
+    assert r == g.EINVAL
+    r = lib.grinqh_decode_vmm_lut(FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, 1, y, y + 64, None)
+    assert r == g.EINVAL and "overlap" in _err(lib)
+    r = lib.grinqh_decode_vmm_lut(FAKE, FAKE + 2, FAKE, 128, 64, 8, thp, lvp, 1, y, None, None)
+    assert r == g.EINVAL and "aligned" in _err(lib)
+    r = lib.grinqh_decode_vmm_lut(FAKE, FAKE, FAKE, 128, 64, 4, thp, lvp, 1, y, None, None)
+    assert r == g.EINVAL and "level" in _err(lib)
