@@ -7,8 +7,10 @@ launch.  The default entry point is ``grinqh_decode_vmm_accumulate`` used the
 way a decode loop uses it: each step adds x W into an output buffer that the
 previous step zeroed, and zeroes the other one for the next step (ping-pong),
 so every step produces a complete y = x W.  ``--mode decode`` times
-``grinqh_decode_vmm`` (deterministic split-K reduction) instead; the default
-run reports both.
+``grinqh_decode_vmm`` (deterministic split-K reduction) instead, and
+``--mode list`` the two-launch form (``grinqh_assign_bits`` then
+``grinqh_vmm`` over the explicit active list); the default run reports all
+three.
 
 Inputs are resident in HBM before timing starts; every step reads a different
 copy of the layer (planes, scales, zeros, x) so that the working set (>= 512
@@ -69,7 +71,8 @@ SWEEP_BMAX = ([f"llama3-8b-gate-4096x14336-bmax6-avg{b}" for b in (3, 4)]
               + [f"llama3-8b-gate-4096x14336-bmax4-avg{b}" for b in (2, 3)]
               + [f"llama3-70b-gate-8192x28672-bmax6-avg{b}" for b in (3, 4)]
               + [f"llama3-70b-gate-8192x28672-bmax4-avg{b}" for b in (2, 3)])
-ENTRY = {"accumulate": "grinqh_decode_vmm_accumulate", "decode": "grinqh_decode_vmm"}
+ENTRY = {"accumulate": "grinqh_decode_vmm_accumulate", "decode": "grinqh_decode_vmm",
+         "list": "grinqh_assign_bits+grinqh_vmm"}
 TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "vmm_traffic_*.md")
 KERNEL_SOURCES = ("decode_stage_gemv_amd/csrc/vmm.hip", "decode_stage_gemv_amd/csrc/bitplane.hpp",
                   "decode_stage_gemv_amd/csrc/common.hpp")
@@ -163,6 +166,10 @@ class Prepared:
         dev = torch.device("cuda:0")
         self.ws = grq.make_workspace(K, N)
         self.y = torch.empty(N, dtype=torch.float32, device=dev)
+        # the two-launch form: assignment buffers
+        self.bits = torch.empty(K, dtype=torch.uint8, device=dev)
+        self.idx = torch.empty(K, dtype=torch.int32, device=dev)
+        self.nact = torch.empty(1, dtype=torch.int32, device=dev)
         self.ybufs = [torch.zeros(N, dtype=torch.float32, device=dev) for _ in range(2)]
         # algorithmic bytes of each copy's step, from the GPU's own assignment
         self.bytes, self.avg_bits = [], []
@@ -182,9 +189,14 @@ class Prepared:
             grq.decode_vmm_accumulate(planes, scales, zeros, x, self.K, self.N, self.thresholds,
                                       self.levels, self.ybufs[k % 2], self.ybufs[(k + 1) % 2],
                                       b_max=self.b_max)
-        else:
+        elif self.mode == "decode":
             grq.decode_vmm(planes, scales, zeros, x, self.K, self.N, self.thresholds, self.levels,
                            self.ws, out=self.y, b_max=self.b_max)
+        else:
+            # assignment and compaction, then the VMM over the explicit list
+            grq.assign_bits(x, self.thresholds, self.levels, self.bits, self.idx, self.nact)
+            grq.vmm(planes, scales, zeros, x, self.bits, self.idx, self.nact, self.K, self.N, self.ws,
+                    out=self.y, b_max=self.b_max)
 
     def run(self, steps, warmup, graph=True):
         """Time `steps` back-to-back steps; returns (ms per step, bytes per step).
@@ -581,7 +593,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch every step from the host")
     ap.add_argument("--mode", choices=sorted(ENTRY), default="accumulate",
                     help="accumulate: grinqh_decode_vmm_accumulate (ping-pong outputs); "
-                         "decode: grinqh_decode_vmm (deterministic split-K)")
+                         "decode: grinqh_decode_vmm (deterministic split-K); "
+                         "list: grinqh_assign_bits then grinqh_vmm (two launches)")
     ap.add_argument("--only", action="store_true", help="time only the chosen entry point")
     ap.add_argument("--copy-probe", action="store_true",
                     help="time a plain 512 MiB device copy (reference for bandwidth and counters)")
