@@ -43,6 +43,7 @@ constexpr int kLThreads = 64 * kLWaves;
 constexpr int kLRowsPerPass = kLThreads / kLWords;   // rows processed per pass (128)
 constexpr int kLMaxRows = 2048;             // rows per workgroup
 constexpr int kLTargetWGs = 512;            // two resident workgroups per CU
+constexpr int kLCopyLoads = 8;              // table loads per thread in flight per round
 constexpr int kLSlices = kTile / kLCols;    // 128-column slices per store tile (8)
 constexpr int kLXCDs = 8;                   // MI355X
 
@@ -132,11 +133,21 @@ void vmm_lut_kernel(LutArgs a) {
 
   // ---- tables of the widths in use -> LDS, one width after another: the
   // 128 columns' tables of width b are one contiguous run in global memory,
-  // copied with loads of up to 16 bytes, all loads of a round issued before
-  // its stores.
+  // copied with loads of up to 16 bytes, all loads of a round (up to 8 per
+  // thread: the 8-bit tables of 128 columns in one round) issued before its
+  // stores.
   if (tid < 9) {
     s_cnt[tid] = 0;
     s_cur[tid] = 0;
+  }
+  // the activations of this thread's rows first, so that their latency
+  // passes under the table copy (rows past the range are clamped, unused)
+  constexpr int kLRowIters = kLMaxRows / kLThreads;
+  uint16_t xpre[kLRowIters];
+#pragma unroll
+  for (int k = 0; k < kLRowIters; ++k) {
+    const int r = tid + k * kLThreads;
+    xpre[k] = a.x[k0 + (r < nrows ? r : 0)];
   }
   {
     const int cols = (int)((N - n0) < kLCols ? (N - n0) : kLCols);      // columns that exist
@@ -154,15 +165,15 @@ void vmm_lut_kernel(LutArgs a) {
         using V = typename std::conditional<kCh == 8, uint4, typename std::conditional<kCh == 4, uint2, uint32_t>::type>::type;
         const V* vs = reinterpret_cast<const V*>(src);
         const int total = cols * nb / kCh;             // loads
-        for (int e0 = 0; e0 < total; e0 += 4 * kLThreads) {
-          V v[4];
+        for (int e0 = 0; e0 < total; e0 += kLCopyLoads * kLThreads) {
+          V v[kLCopyLoads];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
+          for (int k = 0; k < kLCopyLoads; ++k) {
             const int e = e0 + k * kLThreads + tid;
             v[k] = vs[e < total ? e : 0];
           }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
+          for (int k = 0; k < kLCopyLoads; ++k) {
             const int e = e0 + k * kLThreads + tid;
             if (e < total) {
               const int h = e * kCh;                   // first half of this load in the run
@@ -186,12 +197,16 @@ void vmm_lut_kernel(LutArgs a) {
   // every run of 32 entries (a "unit") holds rows of one width
   const AssignRegs ar = load_assign_regs(a.ap);
   __syncthreads();                 // counters cleared
-  for (int r = tid; r < nrows; r += kLThreads) {
-    const uint16_t xv = a.x[k0 + r];
-    const uint32_t b = bits_of(xv, ar);
-    s_xv[r] = xv;
-    s_b[r] = (uint8_t)b;
-    if (b > 0) atomicAdd(&s_cnt[b], 1);
+#pragma unroll
+  for (int k = 0; k < kLRowIters; ++k) {
+    const int r = tid + k * kLThreads;
+    if (r < nrows) {
+      const uint16_t xv = xpre[k];
+      const uint32_t b = bits_of(xv, ar);
+      s_xv[r] = xv;
+      s_b[r] = (uint8_t)b;
+      if (b > 0) atomicAdd(&s_cnt[b], 1);
+    }
   }
   __syncthreads();
   if (tid == 0) {
