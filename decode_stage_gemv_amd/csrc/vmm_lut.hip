@@ -27,6 +27,7 @@
 // tables).  At the end the lanes that share a word are reduced with
 // shuffles, the waves in LDS, and the sums are added into y with fp32
 // atomics (so y accumulates, as the accumulating uniform entry point does).
+#include <atomic>
 #include <type_traits>
 
 #include "bitplane.hpp"
@@ -44,6 +45,7 @@ constexpr int kLRowsPerPass = kLThreads / kLWords;   // rows processed per pass 
 constexpr int kLMaxRows = 2048;             // rows per workgroup
 constexpr int kLTargetWGs = 512;            // two resident workgroups per CU
 constexpr int kLCopyLoads = 8;              // table loads per thread in flight per round
+constexpr int kLMaxDynLds = 160 * 1024 - 1024;   // gfx950: 160 KB of LDS per workgroup, less the static part
 constexpr int kLSlices = kTile / kLCols;    // 128-column slices per store tile (8)
 constexpr int kLXCDs = 8;                   // MI355X
 
@@ -400,12 +402,20 @@ int launch_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x
   if (wgs > 0x7FFFFFFF)
     return fail(GRINQH_EINVAL, "%lld workgroups: more than one launch handles", (long long)wgs);
   const int smem = lut_smem_bytes(a);
-  static bool attr_set = false;
-  if (!attr_set) {
+  if (smem > kLMaxDynLds)
+    return fail(GRINQH_EINVAL, "grinqh_decode_vmm_lut: %d bytes of LDS needed (tables of the levels in use and "
+                               "%d rows), at most %d", smem, a.rows, kLMaxDynLds);
+  // the kernel may take more than the default dynamic LDS: raised once per
+  // device (idempotent, so two threads racing to do it is harmless)
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GRINQH_EDEVICE, "grinqh_decode_vmm_lut: no device");
+  const uint64_t bit = uint64_t(1) << (dev & 63);
+  if (!(attr_done.load(std::memory_order_acquire) & bit)) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(vmm_lut_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLMaxDynLds);
     if (e != hipSuccess) return fail(GRINQH_EDEVICE, "grinqh_decode_vmm_lut: %s", hipGetErrorString(e));
-    attr_set = true;
+    attr_done.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL(vmm_lut_kernel, dim3((unsigned)wgs), dim3(kLThreads), smem, s, a);
   return check_launch("grinqh_decode_vmm_lut");

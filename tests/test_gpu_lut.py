@@ -103,3 +103,13 @@ def test_lut_full_size_sampled_columns():
     r = np.random.default_rng(7)
     cols = np.unique(np.concatenate([r.choice(N, 160, replace=False), [0, 127, 128, 1023, 1024, N - 1]]))
     _run(K, N, 2, 4, 8, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5, cols=cols)
+
+
+def test_lut_largest_lds_use():
+    """Every width in use with 2048 rows per workgroup (one row split across
+    65536 columns): about 143 KB of LDS per workgroup, the most the entry
+    point asks for."""
+    K, N = 2048, 65536
+    r = np.random.default_rng(11)
+    cols = np.unique(np.concatenate([r.choice(N, 96, replace=False), [0, 127, 128, 65535]]))
+    _run(K, N, 5, 7, 8, P_ALL, ALL_LEVELS, cols=cols)
