@@ -10,6 +10,14 @@ Generation" (arXiv 2606.23419).  Each function names the section or equation
 it follows.  Where the paper is silent the plainest reading is taken; each
 such reading is marked "Reading:" below.
 
+Pins: every function here is checked by the CPU tests against something other
+than itself: hand-worked examples (tests/golden/), exact rational brute force
+on small inputs, closed forms (the dense GEMV at full width, zero at width 0,
+a mixture quantile for the thresholds), library routines for special cases
+(NumPy's quantile and packbits) and invariants (nesting, half-bin bound,
+one-hot rows, linearity).  The paper prints no absolute output of the method,
+so none of these pins reproduces a number from the paper itself.
+
 Notation: K input rows (d_in), N output columns (d_out), b_max the bit width
 of the stored codes (8 unless a function is told otherwise; section 3.3
 evaluates b_max in {4, 6, 8}), groups of 128 rows share one (scale, zero) pair
