@@ -48,10 +48,10 @@ constexpr int kMaxRows = kGroup;                 // rows of one workgroup: 128 o
 constexpr int kMaxCouples = kMaxRows / 4 + 6;    // sum over 8 widths of ceil(c_v / 4) <= (128 + 8 * 3) / 4
 constexpr int kRedStride = 33;                   // LDS row stride of the wave reduction
 // Launch shape.  The grid is (row item, column tile) pairs.  Small layers
-// use 64-row items so that more workgroups share the CUs; layers that need
-// more than one round of workgroups use 4-wave workgroups (more of them
-// resident per CU, so one's prologue overlaps another's streaming), the
-// others 8-wave workgroups.
+// use 64-row items so that more workgroups share the CUs; workgroups have 8
+// waves while two fit per CU, 4 waves up to one round of 16 waves per CU,
+// and 2 waves beyond that, so that the largest layers still run in one
+// round (each wave then takes more records, in a rolled loop).
 constexpr int kTargetCUs = 256;                  // MI355X
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;    // buffer offset beyond any range used here
 constexpr int kRsrcWord3 = 0x00020000;           // raw 32-bit buffer, gfx9 family
@@ -67,7 +67,12 @@ VmmGeometry vmm_geometry(int64_t K, int64_t N) {
   g.tiles = n_tiles(N);
   g.rows_per_split = n_groups(K) * g.tiles < kTargetCUs ? 64 : 128;
   g.splits = (K + g.rows_per_split - 1) / g.rows_per_split;
-  g.waves = g.splits * g.tiles > 2 * kTargetCUs ? 4 : 8;
+  // waves per workgroup: 8 while the workgroups fit two per CU, then 4, and
+  // 2 once 4-wave workgroups would need a second round (at four waves per
+  // SIMD a round holds 16 waves per CU): every extra round repeats the
+  // whole latency chain of a workgroup (activations, planes, reduction)
+  const int64_t wgs = g.splits * g.tiles;
+  g.waves = wgs > 4 * kTargetCUs ? 2 : (wgs > 2 * kTargetCUs ? 4 : 8);
   g.partial_floats = g.splits > 1 ? g.splits * padded_cols(N) : 0;
   g.counter_offset = (g.partial_floats * 4 + 255) / 256 * 256;
   g.bytes = g.splits > 1 ? g.counter_offset + g.tiles * 4 : 0;
@@ -220,6 +225,10 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   __shared__ uint32_t s_cx[kWaves][kMaxRecords * 2];      // per wave: record pair -> fp16 x of its rows
   __shared__ float s_hx[2];
   __shared__ int s_last;
+  // 2-wave workgroups: each thread has 8 epilogue columns, whose scales and
+  // zeros are parked in LDS during the record loop (registers are short)
+  constexpr bool kParkScales = kWaves == 2;
+  __shared__ uint32_t s_scz[kParkScales ? kTile : 1];
 
   // workgroup = (column tile, 128-row group), tiles fastest (K, N < 2^31)
   const int tile = blockIdx.x % tiles;
@@ -404,6 +413,10 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   // the prologue's own loads (x, scale, zero) have landed long ago; from here
   // on vmcnt counts only record loads
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if constexpr (kParkScales) {
+#pragma unroll
+    for (int u = 0; u < kCols; ++u) s_scz[tid + u * kVmmThreads] = (uint32_t)sc[u] | ((uint32_t)zr[u] << 16);
+  }
   {
     // Three records in flight.  The record sequence is unrolled (a wave has
     // at most kMaxRecords) so that the load order is static: record j + 3 is
@@ -420,12 +433,28 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       bw[j] = width(j);
       load_record<kMaxRecords>(rr[j], rsrc, src, j, bw[j], pb, lane_off);
     }
+    if constexpr (kMaxRecords <= 12) {
 #pragma unroll
-    for (int j = 0; j < kMaxRecords; ++j) {
-      if (j < nrec) compute_record(rr[j % 3], bw[j % 3], cx[2 * j + h], acc);
-      if (j + 3 < kMaxRecords) {
-        bw[j % 3] = width(j + 3);
-        load_record<kMaxRecords>(rr[j % 3], rsrc, src, j + 3, bw[j % 3], pb, lane_off);
+      for (int j = 0; j < kMaxRecords; ++j) {
+        if (j < nrec) compute_record(rr[j % 3], bw[j % 3], cx[2 * j + h], acc);
+        if (j + 3 < kMaxRecords) {
+          bw[j % 3] = width(j + 3);
+          load_record<kMaxRecords>(rr[j % 3], rsrc, src, j + 3, bw[j % 3], pb, lane_off);
+        }
+      }
+    } else {
+      // too many records to unroll (2-wave workgroups): a rolled loop over
+      // rounds of three, the three register sets in fixed roles, so that the
+      // load order and the wait counts stay static; records past the wave's
+      // last load nothing (width 0)
+      for (int j0 = 0; j0 < nrec; j0 += 3) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const int j = j0 + q;
+          if (j < nrec) compute_record(rr[q], bw[q], cx[2 * j + h], acc);
+          bw[q] = width(j + 3);
+          load_record<kMaxRecords>(rr[q], rsrc, src, j + 3, bw[q], pb, lane_off);
+        }
       }
     }
   }
@@ -458,7 +487,13 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       float A = 0.0f;
 #pragma unroll
       for (int h = 0; h < kWaves; ++h) A += red[(h * 32 + (col >> 5)) * kRedStride + (col & 31)];
-      val[u] = (half_bits_to_float(sc[u]) * sfac) * (A * afac + H) + half_bits_to_float(zr[u]) * X;
+      uint16_t su = sc[u], zu = zr[u];
+      if constexpr (kParkScales) {
+        const uint32_t p = s_scz[col];
+        su = (uint16_t)(p & 0xFFFFu);
+        zu = (uint16_t)(p >> 16);
+      }
+      val[u] = (half_bits_to_float(su) * sfac) * (A * afac + H) + half_bits_to_float(zu) * X;
     }
   }
 
@@ -575,7 +610,9 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_
   a.partials = reinterpret_cast<float*>(ws);
   a.counters = g.bytes > 0 && ws ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + g.counter_offset) : nullptr;
   const dim3 grid((unsigned)(g.splits * g.tiles));
-  if (g.waves == 4)
+  if (g.waves == 2)
+    launch_shape<2>(fused, out_mode, grid, a, s);
+  else if (g.waves == 4)
     launch_shape<4>(fused, out_mode, grid, a, s);
   else
     launch_shape<8>(fused, out_mode, grid, a, s);
