@@ -179,6 +179,9 @@ def test_unpacked_prefill_validation(lib):
     assert lib.grinqh_dense_gemm(FAKE, FAKE, 0, 64, 64, FAKE, None) == g.EINVAL
     assert lib.grinqh_dense_gemm(FAKE, FAKE, 4, 1 << 21, 64, FAKE, None) == g.EINVAL
     assert lib.grinqh_dense_gemm(None, FAKE, 4, 64, 64, FAKE, None) == g.EINVAL
+    assert lib.grinqh_dense_gemm(FAKE, FAKE + 8, 4, 64, 64, FAKE, None) == g.EINVAL   # weights read 16 bytes at a time
+    assert "aligned" in _err(lib)
+    assert lib.grinqh_dense_gemm(FAKE, FAKE, 0, 64, 64, FAKE, None) == g.EINVAL       # an empty batch
 
 
 def test_lut_validation(lib):
