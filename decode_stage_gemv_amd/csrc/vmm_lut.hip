@@ -282,14 +282,13 @@ void vmm_lut_kernel(LutArgs a) {
   // one unit of width B: rebuild the two rows' codes, look both weights of
   // each column up (table index = the code's top B bits), and add
   // x1 w1 + x2 w2 with one fp16 dot into the column's fp32 accumulator
-  auto process = [&](const Unit& t, auto bw) {
+  auto process = [&](const Unit& t, auto bw, uint32_t (&wv)[32]) {
     constexpr int B = decltype(bw)::value;
     constexpr int kStride = (1 << B) + 2;                // halves per column table in LDS
     uint32_t d1[8], d2[8];
     planes_to_codes<B>(t.w1, d1);                        // plane p at code bit 7 - p
     planes_to_codes<B>(t.w2, d2);
     const char* tb = reinterpret_cast<const char*>(s_lut + a.toff[B] + lut_at(32 * wl, 0, kStride));
-    const half2_t xh = __builtin_bit_cast(half2_t, t.xw);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
 #pragma unroll
@@ -307,23 +306,31 @@ void vmm_lut_kernel(LutArgs a) {
         }
         const _Float16 lo = *reinterpret_cast<const _Float16*>(tb + 2 * c * kStride + o1);
         const _Float16 hi = *reinterpret_cast<const _Float16*>(tb + 2 * c * kStride + o2);
-        acc[c] = __builtin_amdgcn_fdot2((half2_t){lo, hi}, xh, acc[c], false);
+        wv[c] = __builtin_bit_cast(uint32_t, (half2_t){lo, hi});
       }
     }
   };
+  // the width-specialised part only produces the weight pairs; the dots
+  // into the accumulators are one piece of code after the switch (inside
+  // every case they made the compiler copy each accumulator per dot)
   auto process_rt = [&](const Unit& t) {
+    uint32_t wv[32];
     switch (t.b) {
-      case 1: process(t, std::integral_constant<int, 1>()); break;
-      case 2: process(t, std::integral_constant<int, 2>()); break;
-      case 3: process(t, std::integral_constant<int, 3>()); break;
-      case 4: process(t, std::integral_constant<int, 4>()); break;
-      case 5: process(t, std::integral_constant<int, 5>()); break;
-      case 6: process(t, std::integral_constant<int, 6>()); break;
-      case 7: process(t, std::integral_constant<int, 7>()); break;
-      case 8: process(t, std::integral_constant<int, 8>()); break;
-      default: break;
+      case 1: process(t, std::integral_constant<int, 1>(), wv); break;
+      case 2: process(t, std::integral_constant<int, 2>(), wv); break;
+      case 3: process(t, std::integral_constant<int, 3>(), wv); break;
+      case 4: process(t, std::integral_constant<int, 4>(), wv); break;
+      case 5: process(t, std::integral_constant<int, 5>(), wv); break;
+      case 6: process(t, std::integral_constant<int, 6>(), wv); break;
+      case 7: process(t, std::integral_constant<int, 7>(), wv); break;
+      case 8: process(t, std::integral_constant<int, 8>(), wv); break;
+      default: return;
     }
+    const half2_t xh = __builtin_bit_cast(half2_t, t.xw);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) acc[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wv[c]), xh, acc[c], false);
   };
+
 
   // two register sets in turn (no copies between them: a register copy of
   // a loaded value would wait for the load), the next unit always in flight
