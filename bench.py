@@ -71,6 +71,9 @@ SWEEP_BMAX = ([f"llama3-8b-gate-4096x14336-bmax6-avg{b}" for b in (3, 4)]
               + [f"llama3-8b-gate-4096x14336-bmax4-avg{b}" for b in (2, 3)]
               + [f"llama3-70b-gate-8192x28672-bmax6-avg{b}" for b in (3, 4)]
               + [f"llama3-70b-gate-8192x28672-bmax4-avg{b}" for b in (2, 3)])
+# workloads whose layer is also timed at two other widths for the marginal bandwidth
+MARGINAL_PAIRS = {"llama3-8b-gate-4096x14336-avg3": ("llama3-8b-gate-4096x14336-avg2",
+                                                     "llama3-8b-gate-4096x14336-avg8")}
 ENTRY = {"accumulate": "grinqh_decode_vmm_accumulate", "decode": "grinqh_decode_vmm",
          "list": "grinqh_assign_bits+grinqh_vmm"}
 TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "vmm_traffic_*.md")
@@ -652,6 +655,28 @@ def main():
             log(f"{args.workload} {ENTRY[mode]}: {m * 1e3:.2f} us/VMM, {others[ENTRY[mode]]['GB_s']:.1f} GB/s")
             del p
 
+    # marginal bandwidth: the same layer at two widths; the difference in
+    # bytes over the difference in time is what streaming a byte costs once
+    # the fixed per-launch cost (dispatch, dependent latencies) is paid
+    marginal = None
+    pair = MARGINAL_PAIRS.get(args.workload)
+    if pair and not args.only:
+        pts = []
+        for name in pair:
+            p = Prepared(name, args.mode, layer=prep.layer)
+            m, b = p.run(args.steps, args.warmup, graph=not args.no_graph)
+            pts.append((name, m * 1e3, b))
+            del p
+        (n_lo, t_lo, b_lo), (n_hi, t_hi, b_hi) = pts
+        bw = (b_hi - b_lo) / ((t_hi - t_lo) * 1e-6) / 1e9 if t_hi > t_lo else None
+        marginal = {"low": {"workload": n_lo, "us_per_vmm": t_lo, "bytes": b_lo},
+                    "high": {"workload": n_hi, "us_per_vmm": t_hi, "bytes": b_hi},
+                    "GB_s": bw, "frac_of_peak": bw / HBM_PEAK_GBS if bw else None,
+                    "fixed_us": t_lo - b_lo / (bw * 1e3) if bw else None}
+        if bw:
+            log(f"marginal bandwidth ({n_lo} -> {n_hi}): {bw:.0f} GB/s ({bw / HBM_PEAK_GBS:.1%} of peak), "
+                f"fixed part {marginal['fixed_us']:.2f} us")
+
     sweep = {}
     names = (SWEEP if args.sweep else []) + (SWEEP_BMAX if args.sweep_bmax else [])
     if names:
@@ -724,6 +749,8 @@ def main():
         "cpu_baseline": cpu,
     }
     out["copy_probe"] = dict(copy, vmm_frac_of_copy=gbs / copy["GB_s_read_plus_write"])
+    if marginal:
+        out["marginal"] = marginal
     if others:
         out["other_entry_points"] = others
     if sweep:
