@@ -2,8 +2,8 @@
 // "Weight Reconstruction and Bias Correction"; Appendix C.1).
 //
 // Work split.  A workgroup owns one column tile (one row tile of the store
-// per row, ct <= 1024 columns) and one 128-row group of K, so every row it
-// touches shares one (scale, zero) row.
+// per row, ct <= 1024 columns) and one item of 128 (or 64) rows inside one
+// 128-row group of K, so every row it touches shares one (scale, zero) row.
 //
 // Row order.  Every wave sees all rows of the group (two per lane) and
 // buckets the active ones by bit width b with ballots, in registers.  Each
@@ -11,8 +11,8 @@
 // a bucket is padded with empty rows: x = 0, no bytes).  A couple is two row
 // pairs; the two 32-lane halves of a wave take one pair each, lane l owning
 // 32 columns (one plane word of each row), so the bit width is the same for
-// the whole wave.  Couple k belongs to wave k mod 8 (its "records", in
-// order).
+// the whole wave.  Couple k belongs to wave k mod W, W the workgroup's
+// waves (8, 4 or 2; its "records", in order).
 //
 // Loads.  A lane loads its pair's plane words straight into registers with
 // 4-byte buffer loads: planes p < b come from the row tile; the loads of
@@ -418,11 +418,13 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     for (int u = 0; u < kCols; ++u) s_scz[tid + u * kVmmThreads] = (uint32_t)sc[u] | ((uint32_t)zr[u] << 16);
   }
   {
-    // Three records in flight.  The record sequence is unrolled (a wave has
-    // at most kMaxRecords) so that the load order is static: record j + 3 is
-    // issued into the registers of record j right after j is consumed, and
-    // the compiler's wait counts let j + 1 and j + 2 stay outstanding.
-    // Records past nrec load nothing (width 0) and are not computed.
+    // Three records in flight.  The record sequence is unrolled (8- and
+    // 4-wave workgroups: at most 5 and 10 records a wave) or rolled over
+    // rounds of three (2-wave workgroups) so that the load order is static:
+    // record j + 3 is issued into the registers of record j right after j is
+    // consumed, and the compiler's wait counts let j + 1 and j + 2 stay
+    // outstanding.  Records past nrec load nothing (width 0) and are not
+    // computed.
     const int h = (tid >> 5) & 1;
     const uint32_t lane_off = 4 * (tid & 31) < pb ? 4u * (uint32_t)(tid & 31) : kOutOfRange;
     auto width = [&](int j) { return j < kMaxRecords ? __builtin_amdgcn_readlane(rec_w, j) : 0; };
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
   for (int c = 0; c < 32; ++c) acc[c] += __shfl_xor(acc[c], 32, 64);
 
-  // ---- reduce the 8 waves in LDS (row stride 33 keeps both the writes and
+  // ---- reduce the waves in LDS (row stride 33 keeps both the writes and
   // the column-wise reads free of bank conflicts)
   const int m = ncp;   // couples (0: no active row)
   float* red = s_red;
