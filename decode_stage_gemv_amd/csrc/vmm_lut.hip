@@ -44,7 +44,6 @@ constexpr int kLThreads = 64 * kLWaves;
 constexpr int kLRowsPerPass = kLThreads / kLWords;   // rows processed per pass (128)
 constexpr int kLMaxRows = 2048;             // rows per workgroup
 constexpr int kLTargetWGs = 512;            // two resident workgroups per CU
-constexpr int kLCopyLoads = 8;              // table loads per thread in flight per round
 constexpr int kLMaxDynLds = 160 * 1024 - 1024;   // gfx950: 160 KB of LDS per workgroup, less the static part
 constexpr int kLSlices = kTile / kLCols;    // 128-column slices per store tile (8)
 constexpr int kLXCDs = 8;                   // MI355X
@@ -62,11 +61,13 @@ struct LutArgs {
   int toff[9];             // LDS offset (halves) of width b's table; -1 if not in use
   int nused;               // widths in use
   int used[8];             // those widths, ascending
+  int lut_bytes;           // size of the table buffer (< 2^31)
   AssignParams ap;
 };
 
 constexpr int kLRedFloats = kLWaves * kLCols;   // wave reduction buffer, aliased on the tables
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr uint32_t kLOutOfRange = 0x7FFFFF00u;  // buffer offset past every range used here
 constexpr int kLRsrcWord3 = 0x00020000;         // raw 32-bit buffer, gfx9 family
 
@@ -133,11 +134,9 @@ void vmm_lut_kernel(LutArgs a) {
   const int bmax = a.bmax;
   const int word0 = (int)(n0 - t0) / 32;
 
-  // ---- tables of the widths in use -> LDS, one width after another: the
-  // 128 columns' tables of width b are one contiguous run in global memory,
-  // copied with loads of up to 16 bytes, all loads of a round (up to 8 per
-  // thread: the 8-bit tables of 128 columns in one round) issued before its
-  // stores.
+  // ---- tables of the widths in use -> LDS: the 128 columns' tables of
+  // width b are one contiguous run in global memory (4-byte aligned: every
+  // table has an even number of entries), copied in 16-byte chunks.
   if (tid < 9) {
     s_cnt[tid] = 0;
     s_cur[tid] = 0;
@@ -152,46 +151,63 @@ void vmm_lut_kernel(LutArgs a) {
     xpre[k] = a.x[k0 + (r < nrows ? r : 0)];
   }
   {
-    const int cols = (int)((N - n0) < kLCols ? (N - n0) : kLCols);      // columns that exist
-    for (int u = 0; u < a.nused; ++u) {
-      const int b = a.used[u];
-      const int nb = 1 << b, stride = nb + 2;
-      const uint16_t* src = a.lut + N * (int64_t)(nb - 2) + n0 * nb;
-      uint16_t* dst = s_lut + a.toff[b];
-      // halves per load: 8 (16 bytes) or 4 when the run is aligned for it
-      // (its start depends on N), else 2
-      const uintptr_t at = reinterpret_cast<uintptr_t>(src);
-      const int ch = (nb >= 8 && at % 16 == 0) ? 8 : (nb >= 4 && at % 8 == 0) ? 4 : 2;
-      auto copy = [&](auto tag) {
-        constexpr int kCh = decltype(tag)::value;        // halves per load
-        using V = typename std::conditional<kCh == 8, uint4, typename std::conditional<kCh == 4, uint2, uint32_t>::type>::type;
-        const V* vs = reinterpret_cast<const V*>(src);
-        const int total = cols * nb / kCh;             // loads
-        for (int e0 = 0; e0 < total; e0 += kLCopyLoads * kLThreads) {
-          V v[kLCopyLoads];
+    // Every width's chunks of this thread are loaded before any is stored
+    // (one memory latency for the whole copy).  The widths are unrolled at
+    // compile time, so shifts and strides are constants; width b takes
+    // max(1, 16 2^b / 512) chunks of 16 bytes per thread, a width not in use
+    // and chunks past the buffer read out of range (zero, no traffic).  The
+    // full 128 columns are copied even where fewer exist: tables of columns
+    // past N feed outputs that are never stored.
+    const __amdgpu_buffer_rsrc_t lrs = lut_rsrc(a.lut, a.lut_bytes);
+    u32x4_t c1[1], c2[1], c3[1], c4[1], c5[1], c6[2], c7[4], c8[8];
+    auto load_w = [&](auto bw, auto& v) {
+      constexpr int B = decltype(bw)::value;
+      constexpr int kChunks = 16 << B;
+      constexpr int kSlots = sizeof(v) / sizeof(v[0]);
+      const bool used = a.toff[B] >= 0;
+      const uint32_t run = (uint32_t)(2 * (N * ((1 << B) - 2) + n0 * (1 << B)));
 #pragma unroll
-          for (int k = 0; k < kLCopyLoads; ++k) {
-            const int e = e0 + k * kLThreads + tid;
-            v[k] = vs[e < total ? e : 0];
-          }
+      for (int k = 0; k < kSlots; ++k) {
+        const int e = k * kLThreads + tid;
+        const uint32_t off = (used && e < kChunks) ? run + 16u * (uint32_t)e : kLOutOfRange;
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(lrs, (int)off, 0, 0);
+      }
+    };
+    auto store_w = [&](auto bw, const auto& v) {
+      constexpr int B = decltype(bw)::value;
+      constexpr int kChunks = 16 << B;
+      constexpr int kSlots = sizeof(v) / sizeof(v[0]);
+      constexpr int nb = 1 << B;
+      if (a.toff[B] < 0) return;
+      uint16_t* dst = s_lut + a.toff[B];
 #pragma unroll
-          for (int k = 0; k < kLCopyLoads; ++k) {
-            const int e = e0 + k * kLThreads + tid;
-            if (e < total) {
-              const int h = e * kCh;                   // first half of this load in the run
-              uint32_t w[4];
-              __builtin_memcpy(w, &v[k], sizeof(V));
-              uint32_t* d = reinterpret_cast<uint32_t*>(dst + lut_at(h >> b, h & (nb - 1), stride));
+      for (int k = 0; k < kSlots; ++k) {
+        const int e = k * kLThreads + tid;
+        if (e < kChunks) {
 #pragma unroll
-              for (int q = 0; q < kCh / 2; ++q) d[q] = w[q];
-            }
+          for (int q = 0; q < 4; ++q) {
+            const int h = 8 * e + 2 * q;                   // half of the run
+            *reinterpret_cast<uint32_t*>(dst + lut_at(h >> B, h & (nb - 1), nb + 2)) = v[k][q];
           }
         }
-      };
-      if (ch == 8) copy(std::integral_constant<int, 8>());
-      else if (ch == 4) copy(std::integral_constant<int, 4>());
-      else copy(std::integral_constant<int, 2>());
-    }
+      }
+    };
+    load_w(std::integral_constant<int, 8>(), c8);
+    load_w(std::integral_constant<int, 7>(), c7);
+    load_w(std::integral_constant<int, 6>(), c6);
+    load_w(std::integral_constant<int, 5>(), c5);
+    load_w(std::integral_constant<int, 4>(), c4);
+    load_w(std::integral_constant<int, 3>(), c3);
+    load_w(std::integral_constant<int, 2>(), c2);
+    load_w(std::integral_constant<int, 1>(), c1);
+    store_w(std::integral_constant<int, 8>(), c8);
+    store_w(std::integral_constant<int, 7>(), c7);
+    store_w(std::integral_constant<int, 6>(), c6);
+    store_w(std::integral_constant<int, 5>(), c5);
+    store_w(std::integral_constant<int, 4>(), c4);
+    store_w(std::integral_constant<int, 3>(), c3);
+    store_w(std::integral_constant<int, 2>(), c2);
+    store_w(std::integral_constant<int, 1>(), c1);
   }
   // ---- activations and widths of this workgroup's rows; the active rows
   // are listed by width: width b's rows fill entries 32 ub[b] .. of the list
@@ -391,6 +407,10 @@ int launch_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x
       off += ((1 << b) + 2) * kLCols + 16 * kLWords;
     }
   for (int u = a.nused; u < 8; ++u) a.used[u] = 8;
+  const int64_t lut_bytes = N * ((int64_t(1) << (bmax + 1)) - 2) * 2;
+  if (lut_bytes >= (int64_t(1) << 31))
+    return fail(GRINQH_EINVAL, "grinqh_decode_vmm_lut: tables of %lld bytes (at most 2^31 - 1)", (long long)lut_bytes);
+  a.lut_bytes = (int)lut_bytes;
   if (off < 2 * kLRedFloats) off = 2 * kLRedFloats;
   a.lut_halves = (off + 7) / 8 * 8;
   a.n_ct = (int)(padded_cols(N) / kLCols);
