@@ -176,11 +176,15 @@ __global__ __launch_bounds__(kGThreads) void dense_gemm_kernel(GemmArgs a) {
       half8_t bf[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) __builtin_memcpy(&bf[cb], b.v[s16][cb], 16);
+      // the wave issuing MFMAs goes first while it does (the other wave on
+      // the SIMD is loading or unpacking): keeps the matrix core fed
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s16 & 1][rb], bf[cb], acc[rb][cb], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
       load_b16(nst, s16, b.v[s16]);
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -270,11 +270,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
         const int row = 128 * wr + 32 * rb + (lane & 31);
         __builtin_memcpy(&af[rb], &s_x[buf][row * kXPitch + 16 * s16 + 8 * (lane >> 5)], 16);
       }
+      // the wave issuing MFMAs goes first while it does (the other wave on
+      // the SIMD is loading or unpacking): keeps the matrix core fed
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
