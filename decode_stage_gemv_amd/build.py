@@ -25,10 +25,11 @@ FLAGS = [
     "-Wno-unused-function",
     # Keep the compiler from emitting packed fp32 arithmetic.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # The first four kernel-argument dwords arrive preloaded in scalar
-    # registers (the VMM puts the activation pointer, K and the tile count
-    # there); without firmware support the kernel loads them itself.
-    "-mllvm", "-amdgpu-kernarg-preload-count=4",
+    # The first nine kernel arguments (as far as they fit the user scalar
+    # registers; a structure argument ends the run) arrive preloaded in
+    # scalar registers: the VMM puts every scalar its prologue needs there.
+    # Without firmware support the kernel loads them itself.
+    "-mllvm", "-amdgpu-kernarg-preload-count=9",
     # Per-kernel register, scratch and occupancy report (checked below).
     "-Rpass-analysis=kernel-resource-usage",
 ]

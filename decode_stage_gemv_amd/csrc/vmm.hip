@@ -210,12 +210,18 @@ enum : int {
   kOutAccumulate = 1  // fp32 device-scope atomic adds into y (y += x W)
 };
 
-// The activation pointer, K and the tile count come first as plain scalars:
-// the build asks for them to be preloaded into scalar registers, so the
-// activation loads can issue before the rest of the arguments arrive.
+// Everything the prologue needs before its first loads (the activation,
+// plane, scale and zero pointers and the shape) comes first as plain
+// scalars: the build asks for the first nine arguments to be preloaded into
+// scalar registers, so the activation and scale loads issue at once instead
+// of after a fetch of the argument block, and that fetch (thresholds,
+// levels) completes while the activations are in flight.
 template <bool kFused, int kOut, int kWaves>
-__global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __restrict__ x, int K, int tiles,
-                                                          VmmArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __restrict__ x,
+                                                          const uint8_t* __restrict__ planes,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint16_t* __restrict__ zeros, int K, int N,
+                                                          int tiles, int rows, int bmax, VmmArgs a) {
   constexpr int kVmmThreads = 64 * kWaves;
   constexpr int kCols = kTile / kVmmThreads;        // output columns per thread in the epilogue
   constexpr int kMaxRecords = (kMaxCouples + kWaves - 1) / kWaves;
@@ -233,8 +239,8 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   // workgroup = (column tile, 128-row group), tiles fastest (K, N < 2^31)
   const int tile = blockIdx.x % tiles;
   const int split = blockIdx.x / tiles;
-  const int k0 = split * a.rows;
-  const int k1 = (k0 + a.rows) < K ? (k0 + a.rows) : K;
+  const int k0 = split * rows;
+  const int k1 = (k0 + rows) < K ? (k0 + rows) : K;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -259,12 +265,10 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   // preloaded arguments, and waits count loads in issue order
   __builtin_amdgcn_sched_barrier(0);
   const AssignRegs ar = load_assign_regs(a.ap);   // scalar registers
-  const int N = (int)a.N;
   const int Np = (N + 127) & ~127;
   const int t0 = tile * kTile;
   const int ct = (Np - t0) < kTile ? (Np - t0) : kTile;   // multiple of 128
   const int pb = ct / 8;                                  // bytes per plane, multiple of 16
-  const int bmax = a.bmax;
   const int rstride = pb * bmax;                          // bytes per row tile
   uint16_t sc[kCols], zr[kCols];
 #pragma unroll
@@ -273,8 +277,8 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     col = col < ct ? col : ct - 1;
     int gc = t0 + col;
     gc = gc < N ? gc : N - 1;
-    sc[u] = a.scales[g * N + gc];
-    zr[u] = a.zeros[g * N + gc];
+    sc[u] = scales[g * N + gc];
+    zr[u] = zeros[g * N + gc];
   }
 
   if constexpr (kFused) {
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 
   // buffer descriptor over this group's row tiles of the tile block
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.planes + store_offset((int64_t)t0 * a.K + (int64_t)k0 * ct, bmax)), (short)0,
+      (void*)(planes + store_offset((int64_t)t0 * K + (int64_t)k0 * ct, bmax)), (short)0,
       (k1 - k0) * rstride, kRsrcWord3);
 
   float acc[32];
@@ -586,17 +590,21 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 template <int kWaves>
 static void launch_shape(bool fused, int out_mode, dim3 grid, const VmmArgs& a, hipStream_t s) {
   const dim3 block(64 * kWaves);
+#define GRINQH_VMM_LAUNCH(F, O)                                                                              \
+  hipLaunchKernelGGL((vmm_kernel<F, O, kWaves>), grid, block, 0, s, a.x, a.planes, a.scales, a.zeros, (int)a.K, \
+                     (int)a.N, a.tiles, a.rows, a.bmax, a)
   if (out_mode == kOutAccumulate) {
     if (fused)
-      hipLaunchKernelGGL((vmm_kernel<true, kOutAccumulate, kWaves>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
+      GRINQH_VMM_LAUNCH(true, kOutAccumulate);
     else
-      hipLaunchKernelGGL((vmm_kernel<false, kOutAccumulate, kWaves>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
+      GRINQH_VMM_LAUNCH(false, kOutAccumulate);
   } else {
     if (fused)
-      hipLaunchKernelGGL((vmm_kernel<true, kOutSplitK, kWaves>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
+      GRINQH_VMM_LAUNCH(true, kOutSplitK);
     else
-      hipLaunchKernelGGL((vmm_kernel<false, kOutSplitK, kWaves>), grid, block, 0, s, a.x, (int)a.K, a.tiles, a);
+      GRINQH_VMM_LAUNCH(false, kOutSplitK);
   }
+#undef GRINQH_VMM_LAUNCH
 }
 
 static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_t s) {
