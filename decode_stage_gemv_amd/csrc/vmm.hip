@@ -130,6 +130,16 @@ __device__ inline float phi_x(int b, int bmax, float x) {
   return (b > 0 && b < bmax) ? x * __builtin_bit_cast(float, (uint32_t)(127 + 7 - b) << 23) : 0.0f;
 }
 
+// Lanes l < 32 get a(l) + a(l + 32), lanes l >= 32 get b(l - 32) + b(l): one
+// swap of the upper half of a with the lower half of b (the swapped values
+// pass through plain integers: a vector element inside a bit cast is
+// mistranslated by the compiler).
+__device__ inline float halves_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+
 // acc[4m + j] += x1 * row1 code + x2 * row2 code for the 32 columns of a lane:
 // bytes [row1 code, 0, row2 code, 0] form two fp16 subnormals c * 2^-24.
 __device__ inline void dot_pair(const uint32_t (&d1)[8], const uint32_t (&d2)[8], half2_t xv, float (&acc)[32]) {
@@ -465,18 +475,18 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  // the two halves of a wave hold the same columns (different pairs)
-#pragma unroll
-  for (int c = 0; c < 32; ++c) acc[c] += __shfl_xor(acc[c], 32, 64);
-
-  // ---- reduce the waves in LDS (row stride 33 keeps both the writes and
-  // the column-wise reads free of bank conflicts)
+  // ---- the two halves of a wave hold the same columns (different pairs):
+  // one lane-half swap per two accumulators leaves column 2c + h of the
+  // lane's word, summed over both halves, in half h; then reduce the waves
+  // in LDS (row stride 33 keeps both the writes and the column-wise reads
+  // free of bank conflicts)
   const int m = ncp;   // couples (0: no active row)
   float* red = s_red;
-  if (lane < 32) {
-    float* dst = red + (wid * 32 + lane) * kRedStride;
+  {
+    const int hh = lane >> 5;
+    float* dst = red + (wid * 32 + (lane & 31)) * kRedStride + hh;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) dst[c] = acc[c];
+    for (int c = 0; c < 16; ++c) dst[2 * c] = halves_sum(acc[2 * c], acc[2 * c + 1]);
   }
   __syncthreads();
   const float H = s_hx[0];
