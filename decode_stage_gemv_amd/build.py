@@ -25,11 +25,12 @@ FLAGS = [
     "-Wno-unused-function",
     # Keep the compiler from emitting packed fp32 arithmetic.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # The first nine kernel arguments (as far as they fit the user scalar
-    # registers; a structure argument ends the run) arrive preloaded in
-    # scalar registers: the VMM puts every scalar its prologue needs there.
-    # Without firmware support the kernel loads them itself.
-    "-mllvm", "-amdgpu-kernarg-preload-count=9",
+    # The leading scalar kernel arguments (up to twelve, as far as they fit
+    # the user scalar registers; a structure argument ends the run) arrive
+    # preloaded in scalar registers: the VMM kernels put every scalar their
+    # prologues need there.  Without firmware support the kernel loads them
+    # itself.
+    "-mllvm", "-amdgpu-kernarg-preload-count=12",
     # Per-kernel register, scratch and occupancy report (checked below).
     "-Rpass-analysis=kernel-resource-usage",
 ]

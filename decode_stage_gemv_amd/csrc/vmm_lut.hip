@@ -99,39 +99,40 @@ __device__ inline int lut_at(int c, int p, int stride) { return c * stride + 16 
 // LDS use allows at most two workgroups (four waves per SIMD) per CU; saying
 // so lets the compiler keep all 32 table lookups of a word in flight.
 __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void vmm_lut_kernel(LutArgs a) {
+void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict__ lutp,
+                    const uint8_t* __restrict__ planesp, int Ki, int Ni, int rows, int splits, int n_ct,
+                    int lut_bytes, int used_mask, int bmax, LutArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t s_dyn[];
   uint16_t* s_lut = s_dyn;
   uint16_t* s_xv = s_dyn + a.lut_halves;
-  uint16_t* s_act = s_xv + a.rows;                            // active rows by width (see below)
-  uint8_t* s_b = reinterpret_cast<uint8_t*>(s_act + a.rows + kLListPad);
+  uint16_t* s_act = s_xv + rows;                              // active rows by width (see below)
+  uint8_t* s_b = reinterpret_cast<uint8_t*>(s_act + rows + kLListPad);
   __shared__ int s_cnt[9], s_cur[9], s_ub[10];
   float* s_red = reinterpret_cast<float*>(s_dyn);   // after the row loop the tables are dead
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t K = a.K, N = a.N;
+  const int64_t K = Ki, N = Ni;
   // workgroup -> (store tile, row split, 128-column slice), slices fastest,
   // then splits: the eight slices of a store tile read the same 128-byte
   // plane lines (16 bytes each) and the splits of a tile the same tables, so
   // consecutive entries of this order are placed on one XCD (hardware
   // workgroup ids go round-robin over the 8 XCDs) and share its L2
   int L = blockIdx.x;
-  const int T = gridDim.x;
+  const int T = (n_ct + kLSlices - 1) / kLSlices * kLSlices * splits;   // the grid (as launched)
   if (T % kLXCDs == 0) L = (L % kLXCDs) * (T / kLXCDs) + L / kLXCDs;
   const int sub = L % kLSlices;
-  const int split = (L / kLSlices) % a.splits;
-  const int cti = (L / kLSlices / a.splits) * kLSlices + sub;
-  if (cti >= a.n_ct) return;       // a slice past a narrow last tile
+  const int split = (L / kLSlices) % splits;
+  const int cti = (L / kLSlices / splits) * kLSlices + sub;
+  if (cti >= n_ct) return;         // a slice past a narrow last tile
   const int64_t n0 = (int64_t)cti * kLCols;
-  const int64_t k0 = (int64_t)split * a.rows;
-  const int nrows = (int)((K - k0) < a.rows ? (K - k0) : a.rows);
+  const int64_t k0 = (int64_t)split * rows;
+  const int nrows = (int)((K - k0) < rows ? (K - k0) : rows);
   const int64_t t0 = n0 / kTile * kTile;
   const int64_t Np = padded_cols(N);
   const int ct = (int)((Np - t0) < kTile ? (Np - t0) : kTile);
   const int pb = ct / 8;
-  const int bmax = a.bmax;
   const int word0 = (int)(n0 - t0) / 32;
 
   // ---- tables of the widths in use -> LDS: the 128 columns' tables of
@@ -148,7 +149,7 @@ void vmm_lut_kernel(LutArgs a) {
 #pragma unroll
   for (int k = 0; k < kLRowIters; ++k) {
     const int r = tid + k * kLThreads;
-    xpre[k] = a.x[k0 + (r < nrows ? r : 0)];
+    xpre[k] = xp[k0 + (r < nrows ? r : 0)];
   }
   {
     // Every width's chunks of this thread are loaded before any is stored
@@ -158,14 +159,19 @@ void vmm_lut_kernel(LutArgs a) {
     // and chunks past the buffer read out of range (zero, no traffic).  The
     // full 128 columns are copied even where fewer exist: tables of columns
     // past N feed outputs that are never stored.
-    const __amdgpu_buffer_rsrc_t lrs = lut_rsrc(a.lut, a.lut_bytes);
+    const __amdgpu_buffer_rsrc_t lrs = lut_rsrc(lutp, lut_bytes);
     u32x4_t c1[1], c2[1], c3[1], c4[1], c5[1], c6[2], c7[4], c8[8];
     auto load_w = [&](auto bw, auto& v) {
       constexpr int B = decltype(bw)::value;
       constexpr int kChunks = 16 << B;
       constexpr int kSlots = sizeof(v) / sizeof(v[0]);
-      const bool used = a.toff[B] >= 0;
-      const uint32_t run = (uint32_t)(2 * (N * ((1 << B) - 2) + n0 * (1 << B)));
+      const bool used = (used_mask >> B) & 1;
+      // wave-uniform, in scalar registers (the buffer is below 2^31 bytes):
+      // a per-lane 64-bit multiply-add here reads an undefined upper half
+      // that the compiler may place in an activation load's register, and
+      // then waits for that load
+      const uint32_t run = __builtin_amdgcn_readfirstlane(
+          2u * ((uint32_t)N * ((1u << B) - 2u) + (uint32_t)n0 * (1u << B)));
 #pragma unroll
       for (int k = 0; k < kSlots; ++k) {
         const int e = k * kLThreads + tid;
@@ -200,6 +206,10 @@ void vmm_lut_kernel(LutArgs a) {
     load_w(std::integral_constant<int, 3>(), c3);
     load_w(std::integral_constant<int, 2>(), c2);
     load_w(std::integral_constant<int, 1>(), c1);
+    // compiler barrier: otherwise the loads of a width sink into the branch
+    // that stores them and are issued only after the earlier widths' stores
+    // (one more memory latency)
+    asm volatile("" ::: "memory");
     store_w(std::integral_constant<int, 8>(), c8);
     store_w(std::integral_constant<int, 7>(), c7);
     store_w(std::integral_constant<int, 6>(), c6);
@@ -260,7 +270,7 @@ void vmm_lut_kernel(LutArgs a) {
   // scalar offset p pb, this lane's word at 4 (word0 + wl)
   const uint32_t rstride = (uint32_t)(pb * bmax);
   const __amdgpu_buffer_rsrc_t prs =
-      lut_rsrc(a.planes + store_offset(t0 * K + k0 * ct, bmax), (int64_t)(nrows > 0 ? nrows : 1) * rstride);
+      lut_rsrc(planesp + store_offset(t0 * K + k0 * ct, bmax), (int64_t)(nrows > 0 ? nrows : 1) * rstride);
   const uint32_t woff = 4u * (uint32_t)(word0 + wl);
   float acc[32];
 #pragma unroll
@@ -444,7 +454,10 @@ int launch_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint16_t* x
     if (e != hipSuccess) return fail(GRINQH_EDEVICE, "grinqh_decode_vmm_lut: %s", hipGetErrorString(e));
     attr_done.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL(vmm_lut_kernel, dim3((unsigned)wgs), dim3(kLThreads), smem, s, a);
+  int used_mask = 0;
+  for (int b = 1; b <= 8; ++b) used_mask |= a.toff[b] >= 0 ? 1 << b : 0;
+  hipLaunchKernelGGL(vmm_lut_kernel, dim3((unsigned)wgs), dim3(kLThreads), smem, s, a.x, a.lut, a.planes, (int)K,
+                     (int)N, a.rows, a.splits, a.n_ct, a.lut_bytes, used_mask, bmax, a);
   return check_launch("grinqh_decode_vmm_lut");
 }
 
