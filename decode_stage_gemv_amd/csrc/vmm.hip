@@ -345,8 +345,9 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   const int ncp = cbv[9];
   const int nrec = ncp > wid ? (ncp - wid + kWaves - 1) / kWaves : 0;   // this wave's couples
 
-  if (wid == 0) {
-    // H = sum x phi and X = sum x over the group's active rows
+  if (wid == kWaves - 1) {
+    // H = sum x phi and X = sum x over the group's active rows (the last
+    // wave has the fewest records, so this stays off the longest path)
     float hs = 0.0f, xs = 0.0f;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
