@@ -93,6 +93,29 @@ int lut_smem_bytes(const LutArgs& a) {
   return a.lut_halves * 2 + a.rows * 2 + (a.rows + kLListPad) * 2 + a.rows + 16;
 }
 
+// Cross-lane sums without LDS traffic.  lut_halves_sum: lanes l < 32 get
+// a(l) + a(l + 32), lanes l >= 32 get b(l - 32) + b(l) (one swap of a's upper
+// half with b's lower half).  lut_rows_sum: with rows of 16 lanes, rows 0
+// and 2 get a's row plus the next row of a, rows 1 and 3 get b's previous
+// row plus its own (one swap of a's odd rows with b's even rows).  Swapped
+// values pass through plain integers: a vector element inside a bit cast is
+// mistranslated by the compiler.
+__device__ inline float lut_halves_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+__device__ inline float lut_rows_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+// The value of the lane kR places further on within its 16-lane row.
+template <int kR>
+__device__ inline float lut_row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + kR, 0xF, 0xF, false));
+}
+
 // LDS position (halves) of entry p of column c in a width-b table block.
 __device__ inline int lut_at(int c, int p, int stride) { return c * stride + 16 * (c >> 5) + p; }
 
@@ -369,20 +392,30 @@ void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict_
     process_rt(tB);
   }
 
-  // ---- reduce: lanes sharing a word (lane bits 2..5), then the waves
+  // ---- reduce over the lanes that share a word (lane bits 2..5), in
+  // registers: a lane-half swap sums accumulator pairs (2q, 2q + 1) over
+  // bit 5, a row swap sums those pairs over bit 4, and two rotations inside
+  // each 16-lane row sum over bits 3 and 2.  Value r then holds, in row rho
+  // (lanes 16 rho ..), column 4 r + {0, 2, 1, 3}[rho] of word lane & 3;
+  // lanes 0..3 of each row write it, then the waves are reduced in LDS
+  float h32[16];
 #pragma unroll
-  for (int c = 0; c < 32; ++c) {
-    float v = acc[c];
-    v += __shfl_xor(v, 4, 64);
-    v += __shfl_xor(v, 8, 64);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    acc[c] = v;
+  for (int q = 0; q < 16; ++q) h32[q] = lut_halves_sum(acc[2 * q], acc[2 * q + 1]);
+  float r16[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    float v = lut_rows_sum(h32[2 * r], h32[2 * r + 1]);
+    v += lut_row_ror<8>(v);
+    v += lut_row_ror<4>(v);
+    r16[r] = v;
   }
   __syncthreads();                 // every wave is done with the tables
-  if (lane < kLWords) {
+  if ((lane & 15) < kLWords) {
+    const int rho = lane >> 4;
+    const int cofs = ((rho & 1) << 1) | (rho >> 1);
+    float* dst = s_red + wid * kLCols + 32 * (lane & 3) + cofs;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) s_red[wid * kLCols + 32 * lane + c] = acc[c];
+    for (int r = 0; r < 8; ++r) dst[4 * r] = r16[r];
   }
   __syncthreads();
   if (tid < kLCols) {
