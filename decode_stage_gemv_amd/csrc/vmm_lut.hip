@@ -84,13 +84,13 @@ __device__ inline __amdgpu_buffer_rsrc_t lut_rsrc(const void* base, int64_t byte
 
 }  // namespace
 
-// LDS: tables, then x (fp16) and the list of active rows (u16 offsets) and
-// widths (u8) of the workgroup's rows, and a counter.
+// LDS: tables, then x (fp16) and the list of active rows (u16 offsets) of
+// the workgroup's rows.
 // The row list holds each width's rows in a run padded to a multiple of 32
 // entries (at most 31 padding entries for each of the 8 widths).
 constexpr int kLListPad = 8 * 32;
 int lut_smem_bytes(const LutArgs& a) {
-  return a.lut_halves * 2 + a.rows * 2 + (a.rows + kLListPad) * 2 + a.rows + 16;
+  return a.lut_halves * 2 + a.rows * 2 + (a.rows + kLListPad) * 2;
 }
 
 // Cross-lane sums without LDS traffic.  lut_halves_sum: lanes l < 32 get
@@ -129,8 +129,7 @@ void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict_
   uint16_t* s_lut = s_dyn;
   uint16_t* s_xv = s_dyn + a.lut_halves;
   uint16_t* s_act = s_xv + rows;                              // active rows by width (see below)
-  uint8_t* s_b = reinterpret_cast<uint8_t*>(s_act + rows + kLListPad);
-  __shared__ int s_cnt[9], s_cur[9], s_ub[10];
+  __shared__ int s_cnt[9], s_cur[9];
   float* s_red = reinterpret_cast<float*>(s_dyn);   // after the row loop the tables are dead
 
   const int tid = threadIdx.x;
@@ -248,40 +247,54 @@ void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict_
   // every run of 32 entries (a "unit") holds rows of one width
   const AssignRegs ar = load_assign_regs(a.ap);
   __syncthreads();                 // counters cleared
+  // widths of this thread's rows (0 past the range), kept in registers
+  uint32_t bk[kLRowIters];
 #pragma unroll
   for (int k = 0; k < kLRowIters; ++k) {
     const int r = tid + k * kLThreads;
+    bk[k] = 0;
     if (r < nrows) {
-      const uint16_t xv = xpre[k];
-      const uint32_t b = bits_of(xv, ar);
-      s_xv[r] = xv;
-      s_b[r] = (uint8_t)b;
-      if (b > 0) atomicAdd(&s_cnt[b], 1);
+      bk[k] = bits_of(xpre[k], ar);
+      s_xv[r] = xpre[k];
     }
   }
-  __syncthreads();
-  if (tid == 0) {
-    int u = 0;
-    for (int b = 1; b <= 8; ++b) {
-      s_ub[b] = u;
-      u += (s_cnt[b] + 31) >> 5;
-    }
-    s_ub[9] = u;
-  }
-  __syncthreads();
-  for (int r = tid; r < nrows; r += kLThreads) {
-    const int b = s_b[r];
-    if (b > 0) s_act[32 * s_ub[b] + atomicAdd(&s_cur[b], 1)] = (uint16_t)r;
-  }
-  if (tid < 8 * 32) {
-    const int b = 1 + (tid >> 5);
-    const int e = s_cnt[b] + (tid & 31);
-    if (e < 32 * (s_ub[b + 1] - s_ub[b])) s_act[32 * s_ub[b] + e] = 0xFFFFu;
-  }
+  // count the rows of each width, then each wave takes the units' starts
+  // from the counts (no per-row widths in LDS: that space would keep the
+  // largest tables from fitting two workgroups per CU)
+#pragma unroll
+  for (int k = 0; k < kLRowIters; ++k)
+    if (bk[k] > 0) atomicAdd(&s_cnt[bk[k]], 1);
   __syncthreads();
   int ub[10];                      // first unit of each width (wave-uniform)
+  {
+    int u = 0;
 #pragma unroll
-  for (int b = 1; b <= 9; ++b) ub[b] = __builtin_amdgcn_readfirstlane(s_ub[b]);
+    for (int v = 1; v <= 8; ++v) {
+      ub[v] = u;
+      u += (__builtin_amdgcn_readfirstlane(s_cnt[v]) + 31) >> 5;
+    }
+    ub[9] = u;
+  }
+  // place every row of non-zero width in its width's run
+#pragma unroll
+  for (int k = 0; k < kLRowIters; ++k) {
+    const uint32_t b = bk[k];
+    if (b > 0) {
+      int first = 0;
+#pragma unroll
+      for (int v = 1; v <= 8; ++v) first = b == (uint32_t)v ? ub[v] : first;
+      s_act[32 * first + atomicAdd(&s_cur[b], 1)] = (uint16_t)(tid + k * kLThreads);
+    }
+  }
+  // pad each width's run to whole units: wave w pads width w + 1
+  static_assert(kLWaves >= 8, "one wave per width");
+#pragma unroll
+  for (int v = 1; v <= 8; ++v) {
+    if (wid + 1 != v) continue;
+    const int e = __builtin_amdgcn_readfirstlane(s_cnt[v]) + lane;
+    if (lane < 32 && e < 32 * (ub[v + 1] - ub[v])) s_act[32 * ub[v] + e] = 0xFFFFu;
+  }
+  __syncthreads();
   const int units = ub[9];
 
   // ---- units: lane = (row pair ps, word wl); a wave takes units wid,
