@@ -8,6 +8,24 @@
 
 namespace grinqh {
 
+// Inclusive prefix sum over the 64 lanes without LDS traffic: shifts by 1,
+// 2, 4, 8 lanes inside each 16-lane row (lanes shifted in from outside the
+// row read 0), then each row adds the totals of the rows below it.
+__device__ inline int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const int lane = threadIdx.x & 63;
+  const int t0 = __builtin_amdgcn_readlane(v, 15);   // row totals
+  const int t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47);
+  v += lane >= 16 ? t0 : 0;
+  v += lane >= 32 ? t1 : 0;
+  v += lane >= 48 ? t2 : 0;
+  return v;
+}
+
 constexpr int kAssignThreads = 1024;
 constexpr int kAssignPerThread = 16;
 
@@ -37,12 +55,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(const uint16_t* 
       const int64_t i = e0 + e;
       if (i < K) bits[i] = (uint8_t)b[e];
     }
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int u = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += u;
-    }
+    const int incl = wave_inclusive_sum(cnt);
     if (lane == 63) wave_tot[wid] = incl;
     __syncthreads();
     int before = 0, chunk_total = 0;

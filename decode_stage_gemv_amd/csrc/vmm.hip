@@ -296,21 +296,18 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     for (int e = 0; e < 2; ++e)
       if (k0 + rq[e] < k1) bq[e] = bits_of(xq[e], ar);
   } else {
-    // the listed rows of this group: positions [p0, p0 + m) of the list
-    __shared__ int s_m, s_p0;
-    if (wid == 0) {
+    // the listed rows of this group: positions [p0, p1) of the list, the
+    // two searches in two waves at once (each is a chain of dependent loads)
+    __shared__ int s_p[2];
+    if (wid < 2) {
       const int64_t n = *a.n_active;
-      const int64_t p0 = wave_lower_bound(a.active_idx, n, k0);
-      const int64_t p1 = wave_lower_bound(a.active_idx, n, k1);
-      int m = (int)(p1 - p0);
-      m = m < 0 ? 0 : (m > kMaxRows ? kMaxRows : m);
-      if (lane == 0) {
-        s_m = m;
-        s_p0 = (int)p0;
-      }
+      const int64_t p = wave_lower_bound(a.active_idx, n, wid == 0 ? k0 : k1);
+      if (lane == 0) s_p[wid] = (int)p;
     }
     __syncthreads();
-    const int m = s_m, p0 = s_p0;
+    const int p0 = s_p[0];
+    int m = s_p[1] - p0;
+    m = m < 0 ? 0 : (m > kMaxRows ? kMaxRows : m);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int q = lane + 64 * e;
