@@ -24,9 +24,10 @@
 // next unit's plane words are in flight while a unit is processed.
 // Workgroups that share a store tile are numbered onto one XCD (its eight
 // 128-column slices read the same plane lines, its row splits the same
-// tables).  At the end the lanes that share a word are reduced with
-// shuffles, the waves in LDS, and the sums are added into y with fp32
-// atomics (so y accumulates, as the accumulating uniform entry point does).
+// tables).  At the end the lanes that share a word are reduced with lane
+// swaps and row rotations in registers, the waves in LDS, and the sums are
+// added into y with fp32 atomics (so y accumulates, as the accumulating
+// uniform entry point does).
 #include <atomic>
 #include <type_traits>
 
