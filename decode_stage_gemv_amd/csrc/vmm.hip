@@ -15,11 +15,12 @@
 // waves (8, 4 or 2; its "records", in order).
 //
 // Loads.  A lane loads its pair's plane words straight into registers with
-// 4-byte buffer loads: planes p < b come from the row tile; the loads of
+// 4-byte buffer loads: planes p < b come from the row tile; a record is 8
+// loads (planes 0..3) or, above width 4, 16, and within those the loads of
 // planes p >= b repeat plane 0 (a cache hit that the width-specialised
-// rebuild ignores) so that every record is the same 16 loads; padding rows
-// use an out-of-range voffset, which returns 0 and moves no bytes.  Only the
-// top b planes of a row are fetched from memory.  Three records are in
+// rebuild ignores); padding rows use an out-of-range voffset, which returns
+// 0 and moves no bytes.  Only the top b planes of a row are fetched from
+// memory.  Three records are in
 // flight per wave; a wave waits only for its own loads and never for another
 // wave until the final reduction.
 //
@@ -160,16 +161,20 @@ struct RecordRegs {
   uint32_t w1[8], w2[8];
 };
 
-// Issue the 16 loads of record j of this wave (width b; b = 0 for a record
-// the wave does not have) into r.  The record's row sources (byte offsets of
-// the row tiles within the group's block, out of range for padding rows)
-// come from the wave's LDS table.  Lane l of a pair loads plane word l of
-// planes p < b of both rows (plane p at scalar offset p pb from the row
-// tile).  Every call issues exactly 16 loads so that the wait counts of the
-// pipeline are the same on every path: the loads of planes p >= b repeat
-// plane 0 (a cache hit; compute_record ignores them), and a padding row or a
-// record the wave does not have uses an out-of-range voffset, which returns
-// 0 and moves no bytes (only the voffset takes part in the range check).
+// Issue the loads of record j of this wave (width b; b = 0 for a record the
+// wave does not have) into r.  The record's row sources (byte offsets of the
+// row tiles within the group's block, out of range for padding rows) come
+// from the wave's LDS table.  Lane l of a pair loads plane word l of planes
+// p < b of both rows (plane p at scalar offset p pb from the row tile).  A
+// record issues 8 loads (planes 0..3 of both rows) or, for b > 4, 16: few
+// shapes of load count keep the compiler's wait counts close to exact (a
+// branch per plane made them wait for nearly everything), and the second
+// half is skipped for the narrow widths that carry most rows; every vector
+// memory instruction costs issue time on the CU even when it moves nothing.
+// Within a half, the loads of planes p >= b repeat plane 0 (a cache hit;
+// compute_record ignores them), and a padding row or a record the wave does
+// not have uses an out-of-range voffset, which returns 0 and moves no bytes
+// (only the voffset takes part in the range check).
 // lane_off is 4 l for the lanes of a word the tile has (4 l < pb) and
 // kOutOfRange for the others, so that a narrow last tile never reads past
 // its own row tiles: the scalar plane offset is not range-checked.
@@ -184,11 +189,19 @@ __device__ inline void load_record(RecordRegs& r, __amdgpu_buffer_rsrc_t rsrc, c
   const uint32_t v1 = s1 == kOutOfRange ? kOutOfRange : s1 + lane_off;
   const uint32_t v2 = s2 == kOutOfRange ? kOutOfRange : s2 + lane_off;
 #pragma unroll
-  for (int p = 0; p < 8; ++p)
+  for (int p = 0; p < 4; ++p)
     r.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)v1, p < b ? p * pb : 0, 0);
 #pragma unroll
-  for (int p = 0; p < 8; ++p)
+  for (int p = 0; p < 4; ++p)
     r.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)v2, p < b ? p * pb : 0, 0);
+  if (b > 4) {
+#pragma unroll
+    for (int p = 4; p < 8; ++p)
+      r.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)v1, p < b ? p * pb : 0, 0);
+#pragma unroll
+    for (int p = 4; p < 8; ++p)
+      r.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)v2, p < b ? p * pb : 0, 0);
+  }
 }
 
 // Rebuild and accumulate one record (width b >= 1, wave-uniform): the
