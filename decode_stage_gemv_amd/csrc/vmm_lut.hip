@@ -314,10 +314,11 @@ void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict_
   for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
 
   // plane words of the lane's two rows in unit u, the unit's width and the
-  // rows' activations as an fp16 pair.  Every load is issued: planes past
-  // the width, padding rows and units past the end use an out-of-range
-  // offset (reads 0, moves no bytes), so the loads need no branch and the
-  // next unit's loads stay in flight while one is processed.
+  // rows' activations as an fp16 pair.  A unit issues 8 loads (planes 0..3)
+  // or, above width 4, 16; within those, planes past the width, padding rows
+  // and units past the end use an out-of-range offset (reads 0, moves no
+  // bytes), so the loads take at most one branch and the next unit's loads
+  // stay in flight while one is processed.
   struct Unit {
     uint32_t w1[8], w2[8];
     uint32_t xw;
@@ -337,9 +338,16 @@ void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict_
     const uint32_t v1 = e1 != 0xFFFFu ? e1 * rstride + woff : kLOutOfRange;
     const uint32_t v2 = e2 != 0xFFFFu ? e2 * rstride + woff : kLOutOfRange;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < 4; ++p) {
       t.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)(p < b ? v1 : kLOutOfRange), p < bmax ? p * pb : 0, 0);
       t.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)(p < b ? v2 : kLOutOfRange), p < bmax ? p * pb : 0, 0);
+    }
+    if (b > 4) {   // planes 4..7 only for the wide units (fewer memory instructions)
+#pragma unroll
+      for (int p = 4; p < 8; ++p) {
+        t.w1[p] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)(p < b ? v1 : kLOutOfRange), p < bmax ? p * pb : 0, 0);
+        t.w2[p] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)(p < b ? v2 : kLOutOfRange), p < bmax ? p * pb : 0, 0);
+      }
     }
   };
   // one unit of width B: rebuild the two rows' codes, look both weights of
