@@ -172,16 +172,17 @@ void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict_
 #pragma unroll
   for (int k = 0; k < kLRowIters; ++k) {
     const int r = tid + k * kLThreads;
-    xpre[k] = xp[k0 + (r < nrows ? r : 0)];
+    xpre[k] = 0;
+    if (k * kLThreads < nrows) xpre[k] = xp[k0 + (r < nrows ? r : 0)];   // no load for a slice past the rows
   }
   {
     // Every width's chunks of this thread are loaded before any is stored
     // (one memory latency for the whole copy).  The widths are unrolled at
     // compile time, so shifts and strides are constants; width b takes
     // max(1, 16 2^b / 512) chunks of 16 bytes per thread, a width not in use
-    // and chunks past the buffer read out of range (zero, no traffic).  The
-    // full 128 columns are copied even where fewer exist: tables of columns
-    // past N feed outputs that are never stored.
+    // issues no loads, and chunks past the buffer read out of range (zero,
+    // no traffic).  The full 128 columns are copied even where fewer exist:
+    // tables of columns past N feed outputs that are never stored.
     const __amdgpu_buffer_rsrc_t lrs = lut_rsrc(lutp, lut_bytes);
     u32x4_t c1[1], c2[1], c3[1], c4[1], c5[1], c6[2], c7[4], c8[8];
     auto load_w = [&](auto bw, auto& v) {
@@ -189,6 +190,7 @@ void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict_
       constexpr int kChunks = 16 << B;
       constexpr int kSlots = sizeof(v) / sizeof(v[0]);
       const bool used = (used_mask >> B) & 1;
+      if (!used) return;           // no load instructions for a width not in use
       // wave-uniform, in scalar registers (the buffer is below 2^31 bytes):
       // a per-lane 64-bit multiply-add here reads an undefined upper half
       // that the compiler may place in an activation load's register, and
