@@ -261,6 +261,34 @@ def test_full_size_sampled_columns(K, N, cfg, mat, P, levels):
     _check_y(bufs[0].cpu().numpy(), lay.codes, lay.scales, lay.zeros, x, bits, cols)
 
 
+EVERY_WIDTH = (0, 1, 2, 3, 4, 5, 6, 7, 8)
+P_EVERY_WIDTH = (0.2, 0.1, 0.1, 0.1, 0.1, 0.1, 0.1, 0.1, 0.1)
+
+
+@pytest.mark.parametrize("K,N,cfg,mat,n_cols", [(1000, 2080, 5, 4, 0), (4096, 4096, 1, 2, 0),
+                                                (8192, 17408, 5, 6, 192)])
+def test_every_width_in_one_launch(K, N, cfg, mat, n_cols):
+    """Levels 0..8 at once (eight thresholds): records of every width, those
+    that load planes 0..3 only and those that also load 4..7, in the 8-wave
+    geometry and (17 column tiles x 64 groups = 1088 workgroups) the 2-wave
+    one, through both fused entry points."""
+    lay = layer(K, N, cfg, mat)
+    th = oracle.calibrate(lay.calib, P_EVERY_WIDTH)
+    x = lay.x[0]
+    bits = oracle.assign(x, th, EVERY_WIDTH)
+    assert set(np.unique(bits).tolist()) == set(range(9))
+    cols = None
+    if n_cols:
+        r = np.random.default_rng(K + N + 1)
+        cols = np.unique(np.concatenate([r.choice(N, n_cols, replace=False), [0, 1023, 1024, N - 1]]))
+    y, planes, _ = _run_decode(lay, x, th, EVERY_WIDTH)
+    _check_y(y, lay.codes, lay.scales, lay.zeros, x, bits, cols)
+    acc = torch.zeros(N, dtype=torch.float32, device="cuda")
+    grq.decode_vmm_accumulate(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), K, N, th, EVERY_WIDTH, acc)
+    torch.cuda.synchronize()
+    _check_y(acc.cpu().numpy(), lay.codes, lay.scales, lay.zeros, x, bits, cols)
+
+
 # ------------------------------------------------------ accumulating entry point
 
 @pytest.mark.parametrize("K,N,cfg,mat,P,levels", [CASES[0], CASES[2], CASES[4], CASES[5], CASES[7], CASES[8], CASES[9]])
