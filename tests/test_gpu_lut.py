@@ -105,6 +105,15 @@ def test_lut_full_size_sampled_columns():
     _run(K, N, 2, 4, 8, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5, cols=cols)
 
 
+def test_lut_70b_gate_sampled_columns():
+    """8192 x 28672 at levels {0, 2, 4, 8}: 2048-row workgroups with the 8-bit
+    table among the widths in use, two per CU."""
+    K, N = 8192, 28672
+    r = np.random.default_rng(13)
+    cols = np.unique(np.concatenate([r.choice(N, 128, replace=False), [0, 127, 128, 1023, 1024, N - 1]]))
+    _run(K, N, 4, 0, 8, synthetic.P_LEVELS_4[3], synthetic.LEVELS_4, cols=cols)
+
+
 def test_lut_largest_lds_use():
     """Every width in use with 2048 rows per workgroup (one row split across
     65536 columns): about 143 KB of LDS per workgroup, the most the entry
