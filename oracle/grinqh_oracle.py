@@ -359,13 +359,15 @@ def vmm_lut(codes, lut, x, bits, b_max: int = B_MAX) -> np.ndarray:
     bits = np.asarray(bits)
     cols = np.arange(N)
     y = np.zeros(N, dtype=np.float64)
+    tables = {}   # each width's tables converted to fp64 once
     for i in np.nonzero(bits > 0)[0]:
         b = int(bits[i])
         if b > b_max:
             raise ValueError(f"row {i}: width {b} above b_max = {b_max}")
         prefix = codes[i] // (1 << (b_max - b))
-        table = np.asarray(lut[b], dtype=np.float64)
-        y += x64[i] * table[cols, prefix]
+        if b not in tables:
+            tables[b] = np.asarray(lut[b], dtype=np.float64)
+        y += x64[i] * tables[b][cols, prefix]
     return y
 
 
@@ -378,10 +380,13 @@ def vmm_lut_abs(codes, lut, x, bits, b_max: int = B_MAX) -> np.ndarray:
     bits = np.asarray(bits)
     cols = np.arange(N)
     out = np.zeros(N, dtype=np.float64)
+    tables = {}   # each width's tables converted to fp64 once
     for i in np.nonzero(bits > 0)[0]:
         b = int(bits[i])
         prefix = codes[i] // (1 << (b_max - b))
-        out += x64[i] * np.abs(np.asarray(lut[b], dtype=np.float64)[cols, prefix])
+        if b not in tables:
+            tables[b] = np.asarray(lut[b], dtype=np.float64)
+        out += x64[i] * np.abs(tables[b][cols, prefix])
     return out
 
 

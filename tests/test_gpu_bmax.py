@@ -154,7 +154,7 @@ def test_level_above_bmax_is_rejected():
                        [1.0], (0, 6), ws, b_max=4)
 
 
-# ------------------------------------------------- full sizes, sampled outputs
+# ------------------------------------------------- full sizes, every output
 
 FULL = [
     (4096, 14336, 2, 4, 6, synthetic.P_BMAX6[4], synthetic.LEVELS_BMAX6),
@@ -164,7 +164,7 @@ FULL = [
 
 
 @pytest.mark.parametrize("K,N,cfg,mat,b_max,P,levels", FULL)
-def test_full_size_bmax_sampled_columns(K, N, cfg, mat, b_max, P, levels):
+def test_full_size_bmax_all_columns(K, N, cfg, mat, b_max, P, levels):
     lay = layer(K, N, cfg, mat, b_max)
     th = oracle.calibrate(lay.calib, P)
     x = lay.x[0]
@@ -174,6 +174,4 @@ def test_full_size_bmax_sampled_columns(K, N, cfg, mat, b_max, P, levels):
                               b_max=b_max)
     torch.cuda.synchronize()
     bits = oracle.assign(x, th, levels)
-    r = np.random.default_rng(K + N + b_max)
-    cols = np.unique(np.concatenate([r.choice(N, 192, replace=False), [0, 31, 32, 1023, 1024, N - 1]]))
-    _check_y(y.cpu().numpy(), lay, x, bits, b_max, cols)
+    _check_y(y.cpu().numpy(), lay, x, bits, b_max)

@@ -229,7 +229,7 @@ def test_deterministic_repeat():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
-# ------------------------------------------------- full sizes, sampled outputs
+# ------------------------------------------------- full sizes, every output
 
 FULL = [
     (4096, 14336, 2, 4, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5),
@@ -241,24 +241,22 @@ FULL = [
 
 
 @pytest.mark.parametrize("K,N,cfg,mat,P,levels", FULL)
-def test_full_size_sampled_columns(K, N, cfg, mat, P, levels):
-    """Both fused entry points at the benchmark shapes: split-K, and the
-    accumulating one in the decode-loop form the benchmark times (add into
-    a zeroed buffer, clear the other)."""
+def test_full_size_all_columns(K, N, cfg, mat, P, levels):
+    """Both fused entry points at the benchmark shapes, every output column:
+    split-K, and the accumulating one in the decode-loop form the benchmark
+    times (add into a zeroed buffer, clear the other)."""
     lay = layer(K, N, cfg, mat)
     th = oracle.calibrate(lay.calib, P)
     x = lay.x[0]
     y, planes, _ = _run_decode(lay, x, th, levels)
     bits = oracle.assign(x, th, levels)
-    r = np.random.default_rng(K + N)
-    cols = np.unique(np.concatenate([r.choice(N, 192, replace=False), [0, 31, 32, 1023, 1024, N - 1]]))
-    _check_y(y, lay.codes, lay.scales, lay.zeros, x, bits, cols)
+    _check_y(y, lay.codes, lay.scales, lay.zeros, x, bits)
     bufs = [torch.zeros(N, dtype=torch.float32, device="cuda"), torch.ones(N, dtype=torch.float32, device="cuda")]
     grq.decode_vmm_accumulate(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), K, N, th, levels,
                               bufs[0], bufs[1])
     torch.cuda.synchronize()
     assert torch.count_nonzero(bufs[1]).item() == 0
-    _check_y(bufs[0].cpu().numpy(), lay.codes, lay.scales, lay.zeros, x, bits, cols)
+    _check_y(bufs[0].cpu().numpy(), lay.codes, lay.scales, lay.zeros, x, bits)
 
 
 EVERY_WIDTH = (0, 1, 2, 3, 4, 5, 6, 7, 8)
