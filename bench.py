@@ -38,6 +38,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 ROT_BYTES = 512 << 20
+MAX_COPIES = 128     # rotated copies of one layer at most (4096 x 4096 at avg 2 needs 114)
 
 # name: (K, N, config, matrix, P key, level set); level sets "b6" and "b4"
 # belong to stores of 6-bit and 4-bit codes (the others to 8-bit codes)
@@ -127,9 +128,14 @@ def measured_traffic(workload, mode):
 
 
 class Layer:
-    """One synthetic layer packed on the GPU, in R rotated copies."""
+    """One synthetic layer packed on the GPU, in R rotated copies.
 
-    def __init__(self, K, N, cfg, mat, b_max=8, copies_bytes=ROT_BYTES):
+    Copies are added on demand (`ensure`): a workload needs enough copies
+    that one cycle through them reads at least ROT_BYTES of data (the bytes
+    its steps actually read, not the size of the store), so no copy can
+    still sit in the 256 MB Infinity Cache when its turn comes again."""
+
+    def __init__(self, K, N, cfg, mat, b_max=8):
         import torch
         import synthetic
         import decode_stage_gemv_amd as grq
@@ -141,15 +147,60 @@ class Layer:
         scales = torch.from_numpy(lay.scales).to(dev)
         zeros = torch.from_numpy(lay.zeros).to(dev)
         self.calib = torch.from_numpy(lay.calib).to(dev)
-        per_copy = planes.numel() + 2 * scales.numel() * 2 + 2 * K
-        self.R = max(1, -(-copies_bytes // per_copy))
-        self.xs_host = synthetic.make_activations(K, self.R, config=cfg, matrix=mat)
-        self.copies = [(planes if r == 0 else planes.clone(), scales.clone(), zeros.clone(),
-                        torch.from_numpy(self.xs_host[r]).to(dev)) for r in range(self.R)]
+        # one activation vector per possible copy, drawn once (copy r uses row r)
+        self.xs_host = synthetic.make_activations(K, MAX_COPIES, config=cfg, matrix=mat)
+        self.copies = [(planes, scales, zeros, torch.from_numpy(self.xs_host[0]).to(dev))]
         self.host = lay
         self.np_cols = int(grq.lib().grinqh_planes_bytes(1, N, 8))
         torch.cuda.synchronize()
-        log(f"layer {K}x{N} (b_max {b_max}): R={self.R} copies, setup {time.time() - t0:.1f}s")
+        log(f"layer {K}x{N} (b_max {b_max}): setup {time.time() - t0:.1f}s")
+
+    @property
+    def R(self):
+        return len(self.copies)
+
+    def ensure(self, R):
+        """Grow to at least R copies (planes, scales, zeros, and a fresh x each)."""
+        import torch
+        if R <= self.R:
+            return
+        if R > MAX_COPIES:
+            raise ValueError(f"{R} rotated copies requested, at most {MAX_COPIES}")
+        dev = torch.device("cuda:0")
+        planes, scales, zeros, _ = self.copies[0]
+        for r in range(self.R, R):
+            self.copies.append((planes.clone(), scales.clone(), zeros.clone(),
+                                torch.from_numpy(self.xs_host[r]).to(dev)))
+        torch.cuda.synchronize()
+        log(f"layer {self.K}x{self.N}: {self.R} rotated copies")
+
+
+def rotation_copies(bytes_per_step):
+    """Copies needed so that one cycle reads at least ROT_BYTES (twice the
+    256 MB Infinity Cache) of the bytes the steps actually read."""
+    return max(2, -(-ROT_BYTES // max(int(bytes_per_step), 1)))
+
+
+_SCRUB = {}
+
+
+def scrub_init():
+    """Allocate and fill the scrub buffer once, long before any timed region
+    (the fill leaves dirty lines in the Infinity Cache; their write-back must
+    not land inside a measurement)."""
+    import torch
+    if "buf" not in _SCRUB:
+        _SCRUB["buf"] = torch.ones(ROT_BYTES // 4, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+
+def scrub_cache():
+    """Read 512 MiB (twice the 256 MB Infinity Cache) so that nothing a timed
+    region reads is still cached from an earlier pass over the same copies.
+    A read, not a write: evicting clean lines costs nothing later, while
+    written lines would be written back during the next timed region."""
+    scrub_init()
+    _SCRUB["sum"] = _SCRUB["buf"].sum()
 
 
 class Prepared:
@@ -164,8 +215,11 @@ class Prepared:
         self.b_max = bmax_of(lv)
         self.layer = layer if layer is not None else Layer(K, N, cfg, mat, self.b_max)
         assert self.layer.b_max == self.b_max
-        self.R = self.layer.R
         self.thresholds = [float(v) for v in grq.calibrate(self.layer.calib, self.P).cpu().numpy()]
+        # size the rotation by the bytes a step of this workload reads
+        b0, _ = algorithmic_bytes(self.layer.copies[0][3], K, N, self.thresholds, self.levels, self.layer.np_cols)
+        self.layer.ensure(rotation_copies(0.9 * b0))
+        self.R = self.layer.R
         dev = torch.device("cuda:0")
         self.ws = grq.make_workspace(K, N)
         self.y = torch.empty(N, dtype=torch.float32, device=dev)
@@ -181,8 +235,10 @@ class Prepared:
             self.bytes.append(nb)
             self.avg_bits.append(avg)
         torch.cuda.synchronize()
+        self.touched_per_cycle = float(np.sum(self.bytes))
         log(f"prepared {name} ({ENTRY[mode]}): avg bits {np.mean(self.avg_bits):.3f}, "
-            f"{np.mean(self.bytes) / 1e6:.2f} MB/step")
+            f"{np.mean(self.bytes) / 1e6:.2f} MB/step, {self.R} copies, "
+            f"{self.touched_per_cycle / 1e6:.0f} MB read per rotation cycle")
 
     def step(self, k):
         import decode_stage_gemv_amd as grq
@@ -221,6 +277,7 @@ class Prepared:
                     for k in range(steps):
                         self.step(k)
                 g.replay()                      # warm replay
+                scrub_cache()
                 s.synchronize()
                 start = torch.cuda.Event(enable_timing=True)
                 stop = torch.cuda.Event(enable_timing=True)
@@ -231,6 +288,7 @@ class Prepared:
             ms = start.elapsed_time(stop) / steps
         else:
             stream = torch.cuda.current_stream()
+            scrub_cache()
             start = torch.cuda.Event(enable_timing=True)
             stop = torch.cuda.Event(enable_timing=True)
             start.record(stream)
@@ -400,6 +458,7 @@ def _graph_time(fn, steps, warmup):
             for _ in range(steps):
                 fn()
         g.replay()
+        scrub_cache()
         s.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
@@ -490,19 +549,21 @@ def lut_bench(name, steps=100, warmup=10):
     lut = torch.from_numpy(synthetic.lut_flat(tables, N, b_max)).to(dev)
     calib = torch.from_numpy(synthetic.make_calibration(K, config=cfg, matrix=mat)).to(dev)
     th = [float(v) for v in grq.calibrate(calib, P).cpu().numpy()]
-    per_copy = planes.numel() + 2 * lut.numel() + 2 * K
-    R = max(1, -(-ROT_BYTES // per_copy))
-    xs = synthetic.make_activations(K, R, config=cfg, matrix=mat)
+    xs = synthetic.make_activations(K, MAX_COPIES, config=cfg, matrix=mat)
+    used = sorted(set(int(v) for v in levels if v > 0))
+    lut_bytes = sum(N * (1 << b) * 2 for b in used)
+    np_cols = int(grq.lib().grinqh_planes_bytes(1, N, 8))
+
+    def nbytes(x):
+        bits, _, _ = grq.assign_bits(x, th, levels)
+        return int(bits.to(torch.int64).sum().item()) * np_cols // 8 + lut_bytes + 2 * K
+
+    # rotation sized by the bytes a step reads (planes of its widths, tables, x)
+    R = rotation_copies(0.9 * nbytes(torch.from_numpy(xs[0]).to(dev)))
     copies = [(planes if r == 0 else planes.clone(), lut if r == 0 else lut.clone(),
                torch.from_numpy(xs[r]).to(dev)) for r in range(R)]
     ybufs = [torch.zeros(N, dtype=torch.float32, device=dev) for _ in range(2)]
-    used = sorted(set(int(v) for v in levels if v > 0))
-    lut_bytes = sum(N * (1 << b) * 2 for b in used)
-    step_bytes = []
-    np_cols = int(grq.lib().grinqh_planes_bytes(1, N, 8))
-    for (_, _, x) in copies:
-        bits, _, _ = grq.assign_bits(x, th, levels)
-        step_bytes.append(int(bits.to(torch.int64).sum().item()) * np_cols // 8 + lut_bytes + 2 * K)
+    step_bytes = [nbytes(x) for (_, _, x) in copies]
     state = {"k": 0}
 
     def step():
@@ -511,11 +572,13 @@ def lut_bench(name, steps=100, warmup=10):
         pl, lt, x = copies[k % R]
         grq.decode_vmm_lut(pl, lt, x, K, N, th, levels, ybufs[k % 2], ybufs[(k + 1) % 2], b_max=b_max)
 
-    log(f"lut layer {K}x{N} (b_max {b_max}): R={R} copies, setup {time.time() - t_setup:.1f}s")
+    log(f"lut layer {K}x{N} (b_max {b_max}): R={R} copies ({sum(step_bytes) / 1e6:.0f} MB read per cycle), "
+        f"setup {time.time() - t_setup:.1f}s")
     us = _graph_time(step, steps, warmup)
     b = float(np.mean([step_bytes[k % R] for k in range(steps)]))
     out = {"workload": name, "entry_point": "grinqh_decode_vmm_lut", "us_per_vmm": us,
-           "GB_s": b / (us * 1e-6) / 1e9, "bytes_per_step": b, "table_bytes_per_step": lut_bytes}
+           "GB_s": b / (us * 1e-6) / 1e9, "bytes_per_step": b, "table_bytes_per_step": lut_bytes,
+           "rotated_copies": R, "touched_bytes_per_cycle": float(sum(step_bytes))}
     out["frac_of_peak"] = out["GB_s"] / HBM_PEAK_GBS
     log(f"{name} grinqh_decode_vmm_lut: {us:.2f} us/VMM, {out['GB_s']:.1f} GB/s ({out['frac_of_peak']:.1%})")
     return out
@@ -588,8 +651,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the bit-width sweep (4096^2, 4096x14336, 70B gate at 0.5..8 bits)")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false",
+                    help="skip the bit-width sweep (4096^2 and 4096x14336 at avg 2/3/4/8, 70B gate at 0.5..8 bits)")
     ap.add_argument("--sweep-bmax", action="store_true",
                     help="also time stores of 6-bit and 4-bit codes (4096x14336 and 70B gate)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -621,6 +684,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    scrub_init()
     if args.copy_probe:
         print(json.dumps({"copy_probe": copy_probe()}), flush=True)
         return
@@ -655,47 +719,35 @@ def main():
             log(f"{args.workload} {ENTRY[mode]}: {m * 1e3:.2f} us/VMM, {others[ENTRY[mode]]['GB_s']:.1f} GB/s")
             del p
 
-    # marginal bandwidth: the same layer at two widths; the difference in
-    # bytes over the difference in time is what streaming a byte costs once
-    # the fixed per-launch cost (dispatch, dependent latencies) is paid
-    marginal = None
-    pair = MARGINAL_PAIRS.get(args.workload)
-    if pair and not args.only:
-        pts = []
-        for name in pair:
-            p = Prepared(name, args.mode, layer=prep.layer)
-            m, b = p.run(args.steps, args.warmup, graph=not args.no_graph)
-            pts.append((name, m * 1e3, b))
-            del p
-        (n_lo, t_lo, b_lo), (n_hi, t_hi, b_hi) = pts
-        bw = (b_hi - b_lo) / ((t_hi - t_lo) * 1e-6) / 1e9 if t_hi > t_lo else None
-        marginal = {"low": {"workload": n_lo, "us_per_vmm": t_lo, "bytes": b_lo},
-                    "high": {"workload": n_hi, "us_per_vmm": t_hi, "bytes": b_hi},
-                    "GB_s": bw, "frac_of_peak": bw / HBM_PEAK_GBS if bw else None,
-                    "fixed_us": t_lo - b_lo / (bw * 1e3) if bw else None}
-        if bw:
-            log(f"marginal bandwidth ({n_lo} -> {n_hi}): {bw:.0f} GB/s ({bw / HBM_PEAK_GBS:.1%} of peak), "
-                f"fixed part {marginal['fixed_us']:.2f} us")
-
+    # the metric's sweep: 4096 x 4096 and 4096 x 14336 at avg 2/3/4/8 bits and
+    # the 70B gate at 0.5..8 bits (the headline layer is reused, not redrawn)
     sweep = {}
-    names = (SWEEP if args.sweep else []) + (SWEEP_BMAX if args.sweep_bmax else [])
+    names = [] if args.only else (SWEEP if args.sweep else []) + (SWEEP_BMAX if args.sweep_bmax else [])
     if names:
-        layers = {}
+        layers = {(prep.K, prep.N, prep.layer.cfg, prep.layer.mat, prep.b_max): prep.layer}
         for name in names:
             K, N, cfg, mat, _, lv = WORKLOADS[name]
             key = (K, N, cfg, mat, bmax_of(lv))
             if key not in layers:
-                layers.clear()
+                for k in [k for k in layers if layers[k] is not prep.layer]:
+                    del layers[k]
                 torch.cuda.empty_cache()
                 layers[key] = Layer(K, N, cfg, mat, bmax_of(lv))
-            p = Prepared(name, args.mode, layer=layers[key])
-            m, b = p.run(min(args.steps, 100), args.warmup)
+            if name == args.workload:
+                m, b, p = ms, step_bytes, prep
+            else:
+                p = Prepared(name, args.mode, layer=layers[key])
+                m, b = p.run(min(args.steps, 100), args.warmup, graph=not args.no_graph)
             sweep[name] = {"us_per_vmm": m * 1e3, "GB_s": b / (m * 1e-3) / 1e9,
                            "frac_of_peak": b / (m * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                           "avg_bits": float(np.mean(p.avg_bits)), "bytes": b}
-            log(f"{name}: {m * 1e3:.2f} us/VMM, {sweep[name]['GB_s']:.1f} GB/s, avg bits {sweep[name]['avg_bits']:.2f}")
-            del p
+                           "avg_bits": float(np.mean(p.avg_bits)), "bytes": b,
+                           "rotated_copies": p.R, "touched_bytes_per_cycle": p.touched_per_cycle}
+            log(f"{name}: {m * 1e3:.2f} us/VMM, {sweep[name]['GB_s']:.1f} GB/s "
+                f"({sweep[name]['frac_of_peak']:.1%}), avg bits {sweep[name]['avg_bits']:.2f}")
+            if p is not prep:
+                del p
         layers.clear()
+        torch.cuda.empty_cache()
         fit_pts = [(v["bytes"], v["us_per_vmm"]) for k, v in sweep.items() if k.startswith("llama3-70b-gate-8192x28672-avg")]
         if len(fit_pts) >= 3:
             sweep["linear_fit_70b_gate"] = linear_fit(fit_pts)
@@ -705,6 +757,24 @@ def main():
             # one line over every shape of the sweep (4096^2, 4096x14336, 70B gate)
             sweep["linear_fit_all_shapes"] = linear_fit(all_pts)
             log(f"linear fit over all swept shapes: {sweep['linear_fit_all_shapes']}")
+
+    # marginal bandwidth: the same layer at two widths; the difference in
+    # bytes over the difference in time is what streaming a byte costs once
+    # the fixed per-launch cost (dispatch, dependent latencies) is paid
+    marginal = None
+    pair = MARGINAL_PAIRS.get(args.workload)
+    if pair and all(n in sweep for n in pair):
+        (n_lo, n_hi) = pair
+        t_lo, b_lo = sweep[n_lo]["us_per_vmm"], sweep[n_lo]["bytes"]
+        t_hi, b_hi = sweep[n_hi]["us_per_vmm"], sweep[n_hi]["bytes"]
+        bw = (b_hi - b_lo) / ((t_hi - t_lo) * 1e-6) / 1e9 if t_hi > t_lo else None
+        marginal = {"low": {"workload": n_lo, "us_per_vmm": t_lo, "bytes": b_lo},
+                    "high": {"workload": n_hi, "us_per_vmm": t_hi, "bytes": b_hi},
+                    "GB_s": bw, "frac_of_peak": bw / HBM_PEAK_GBS if bw else None,
+                    "fixed_us": t_lo - b_lo / (bw * 1e3) if bw else None}
+        if bw:
+            log(f"marginal bandwidth ({n_lo} -> {n_hi}): {bw:.0f} GB/s ({bw / HBM_PEAK_GBS:.1%} of peak), "
+                f"fixed part {marginal['fixed_us']:.2f} us")
 
     prefill = None
     if args.prefill_tokens > 0 and not args.only:
@@ -741,7 +811,8 @@ def main():
         "config": {"workload": args.workload, "entry_point": ENTRY[args.mode], "K": prep.K, "N": prep.N,
                    "b_max": prep.b_max,
                    "avg_bits": float(np.mean(prep.avg_bits)), "bytes_per_step": step_bytes,
-                   "rotated_copies": prep.R, "graph_replay": not args.no_graph,
+                   "rotated_copies": prep.R, "touched_bytes_per_cycle": prep.touched_per_cycle,
+                   "cache_scrub_read_bytes_before_timing": ROT_BYTES, "graph_replay": not args.no_graph,
                    "arithmetic": "fp16 x times codes (as fp16 subnormals) into fp32 accumulators, fp32 dequant",
                    "thresholds": prep.thresholds, "levels": list(prep.levels)},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -204,8 +204,13 @@ def _check_layer(planes, scales, zeros, x, K, N, b_max):
 
 def vmm(planes, scales, zeros, x, bits, active_idx, n_active, K: int, N: int, workspace,
         out=None, stream=None, b_max: int = MAX_BITS):
-    """y fp32 [N] from an explicit assignment (bits, active list, its length)."""
+    """y fp32 [N] from an explicit assignment (bits, active list, its length).
+
+    active_idx must hold K entries (the kernel clamps the device-side count to
+    [0, K] and may read any of them)."""
     import torch
+    if not isinstance(active_idx, torch.Tensor) or active_idx.numel() < K:
+        raise ValueError(f"active_idx must be a tensor of at least K = {K} entries")
     _check_layer(planes, scales, zeros, x, K, N, b_max)
     _dev(bits, "bits", torch.uint8, (K,))
     _dev(active_idx, "active_idx", torch.int32)

@@ -18,6 +18,8 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
+void clear_error() { g_last_error[0] = 0; }
+
 int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GRINQH_EDEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -27,7 +29,7 @@ int check_launch(const char* what) {
 static inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // max_level: the widest level allowed (8, or the store's b_max for the fused VMM).
-static int check_assign_params(const float* thresholds, const uint8_t* levels, int n, int max_level,
+int check_assign_params(const float* thresholds, const uint8_t* levels, int n, int max_level,
                                AssignParams* ap) {
   if (n < 0 || n > kMaxThresholds) return fail(GRINQH_EINVAL, "n = %d thresholds, expected 0..%d", n, kMaxThresholds);
   if (n > 0 && !thresholds) return fail(GRINQH_EINVAL, "thresholds is NULL");
@@ -63,7 +65,7 @@ static int check_shape(int64_t K, int64_t N, int b_max) {
   return GRINQH_OK;
 }
 
-static int check_layer(const void* planes, const void* scales, const void* zeros, const void* x,
+int check_layer(const void* planes, const void* scales, const void* zeros, const void* x,
                        const void* y, int64_t K, int64_t N, int b_max) {
   if (!planes || !scales || !zeros || !x || !y) return fail(GRINQH_EINVAL, "NULL data pointer");
   return check_shape(K, N, b_max);

@@ -63,9 +63,13 @@ __device__ inline uint32_t bits_of(uint16_t xh, const AssignRegs& r) {
   return (uint32_t)b;
 }
 
-// Host-side status plumbing (api.hip).
+// Host-side status plumbing and argument checks (api.hip).
 int fail(int status, const char* fmt, ...);
 int check_launch(const char* what);
+void clear_error();
+int check_layer(const void* planes, const void* scales, const void* zeros, const void* x, const void* y,
+                int64_t K, int64_t N, int b_max);
+int check_assign_params(const float* thresholds, const uint8_t* levels, int n, int max_level, AssignParams* ap);
 
 // Workspace geometry used by the VMM kernels and grinqh_workspace_bytes.
 struct VmmGeometry {
@@ -92,6 +96,11 @@ int launch_vmm_list(const uint8_t* planes, const uint16_t* scales, const uint16_
 int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                      const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
                      float* y, void* ws, hipStream_t s);
+// The fused split-K VMM with the partial rows and tile counters given apart
+// (the allocation-free entry point keeps them in a fixed device array).
+int launch_vmm_fused_split(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                           const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
+                           float* y, float* partials, unsigned* counters, hipStream_t s);
 int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                           const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
                           float* y, float* clear, hipStream_t s);

@@ -313,7 +313,10 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     // two searches in two waves at once (each is a chain of dependent loads)
     __shared__ int s_p[2];
     if (wid < 2) {
-      const int64_t n = *a.n_active;
+      // a count outside [0, K] (not from a well-formed list) is clamped, so
+      // the searches stay inside the K entries the list buffer must hold
+      int64_t n = *a.n_active;
+      n = n < 0 ? 0 : (n > a.K ? a.K : n);
       const int64_t p = wave_lower_bound(a.active_idx, n, wid == 0 ? k0 : k1);
       if (lane == 0) s_p[wid] = (int)p;
     }
@@ -426,6 +429,14 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       }
     }
   }
+
+  // The record tables were written above by whichever lanes own the rows and
+  // are read below by the other lanes of the same wave: a wave-scope fence
+  // orders the LDS writes before the reads, and the wave barrier keeps the
+  // compiler from moving either across this point.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // buffer descriptor over this group's row tiles of the tile block
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -561,10 +572,21 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     }
 
     // ---- the last workgroup of the tile adds the partial rows in split
-    // order.  No cache-wide fence: each wave waits until its device-scope
-    // stores are acknowledged, the barrier makes that true for the whole
-    // workgroup, and only then is the tile counter bumped; the workgroup that
-    // sees the final count reads the partial rows with device-scope loads.
+    // order.  Ordering argument (no cache-wide fence, which would write back
+    // and invalidate the whole L2 of every XCD):
+    //  1. the partial stores above are device-scope: they go through the
+    //     XCD's L2 to the level that every XCD reads, and the wait below
+    //     returns only once the memory system has acknowledged each of them;
+    //  2. the barrier makes (1) hold for every wave of the workgroup before
+    //     thread 0 bumps the tile counter (a device-scope atomic, performed
+    //     at that same level), so a count of c means c workgroups' partials
+    //     are already visible there;
+    //  3. the workgroup that reads the final count learns it through LDS
+    //     after a second barrier, so its partial loads are issued only after
+    //     the atomic returned, and they are device-scope loads, which miss the
+    //     XCD's own L2 and read that level.
+    // Relaxed atomics plus acknowledged stores and this control dependence
+    // give the order an acquire/release pair would give at agent scope.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -608,6 +630,13 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   }
 }
 
+// The caller's workspace: partial rows first, the per-tile counters after them.
+static float* ws_partials(void* ws) { return reinterpret_cast<float*>(ws); }
+static unsigned* ws_counters(void* ws, int64_t K, int64_t N) {
+  const VmmGeometry g = vmm_geometry(K, N);
+  return g.bytes > 0 && ws ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + g.counter_offset) : nullptr;
+}
+
 template <int kWaves>
 static void launch_shape(bool fused, int out_mode, dim3 grid, const VmmArgs& a, hipStream_t s) {
   const dim3 block(64 * kWaves);
@@ -628,7 +657,8 @@ static void launch_shape(bool fused, int out_mode, dim3 grid, const VmmArgs& a, 
 #undef GRINQH_VMM_LAUNCH
 }
 
-static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_t s) {
+// partials/counters: the split-K workspace (both NULL in accumulate mode).
+static int launch_vmm(bool fused, int out_mode, VmmArgs& a, float* partials, unsigned* counters, hipStream_t s) {
   const VmmGeometry g = vmm_geometry(a.K, a.N);
   if (g.splits * g.tiles > 0x7FFFFFFF)
     return fail(GRINQH_EINVAL, "%lld workgroups: more than one launch handles", (long long)(g.splits * g.tiles));
@@ -638,8 +668,8 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, void* ws, hipStream_
   a.splits = (int)g.splits;
   a.tiles = (int)g.tiles;
   a.rows = (int)g.rows_per_split;
-  a.partials = reinterpret_cast<float*>(ws);
-  a.counters = g.bytes > 0 && ws ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + g.counter_offset) : nullptr;
+  a.partials = partials;
+  a.counters = counters;
   const dim3 grid((unsigned)(g.splits * g.tiles));
   if (g.waves == 2)
     launch_shape<2>(fused, out_mode, grid, a, s);
@@ -659,7 +689,7 @@ int launch_vmm_list(const uint8_t* planes, const uint16_t* scales, const uint16_
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.bits = bits; a.active_idx = active_idx; a.n_active = n_active;
   a.y = y; a.K = K; a.N = N; a.bmax = bmax;
-  return launch_vmm(false, kOutSplitK, a, ws, s);
+  return launch_vmm(false, kOutSplitK, a, ws_partials(ws), ws_counters(ws, K, N), s);
 }
 
 int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
@@ -668,7 +698,16 @@ int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.y = y; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
-  return launch_vmm(true, kOutSplitK, a, ws, s);
+  return launch_vmm(true, kOutSplitK, a, ws_partials(ws), ws_counters(ws, K, N), s);
+}
+
+int launch_vmm_fused_split(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                           const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
+                           float* y, float* partials, unsigned* counters, hipStream_t s) {
+  VmmArgs a{};
+  a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
+  a.y = y; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
+  return launch_vmm(true, kOutSplitK, a, partials, counters, s);
 }
 
 int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
@@ -677,7 +716,7 @@ int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const u
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.y = y; a.clear = clear; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
-  return launch_vmm(true, kOutAccumulate, a, nullptr, s);
+  return launch_vmm(true, kOutAccumulate, a, nullptr, nullptr, s);
 }
 
 }  // namespace grinqh

@@ -200,3 +200,17 @@ def test_lut_validation(lib):
     assert r == g.EINVAL and "aligned" in _err(lib)
     r = lib.grinqh_decode_vmm_lut(FAKE, FAKE, FAKE, 128, 64, 4, thp, lvp, 1, y, None, None)
     assert r == g.EINVAL and "level" in _err(lib)
+
+
+def test_list_vmm_binding_requires_a_full_length_list():
+    """The list entry point's kernel clamps the device-side count to [0, K]
+    and may read any of the first K list entries, so the binding refuses a
+    list buffer shorter than K before touching the device."""
+    import torch
+    import decode_stage_gemv_amd as grq
+    K, N = 256, 64
+    short = torch.zeros(K - 1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="active_idx"):
+        grq.vmm(None, None, None, None, None, short, None, K, N, None)
+    with pytest.raises(ValueError, match="active_idx"):
+        grq.vmm(None, None, None, None, None, [0] * K, None, K, N, None)

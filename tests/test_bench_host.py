@@ -56,3 +56,14 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_rotation_is_sized_by_bytes_read():
+    """One cycle through the copies reads at least 512 MiB (twice the 256 MB
+    Infinity Cache), counting the bytes a step reads, not the store's size."""
+    for step_bytes in (4.72e6, 16.4e6, 23.76e6, 22.5e6, 242e6, 6e8):
+        R = bench.rotation_copies(step_bytes)
+        assert R * step_bytes >= bench.ROT_BYTES
+        assert (R - 1) * step_bytes < bench.ROT_BYTES or R == 2
+        assert R <= bench.MAX_COPIES
+    assert bench.rotation_copies(23.76e6) == 23
