@@ -9,7 +9,7 @@ call raises.
 
 Names follow the C ABI in ``include/grinqh.h``:
 ``pack``, ``calibrate``, ``assign_bits``, ``vmm``, ``decode_vmm``,
-``decode_vmm_accumulate``, ``decode_vmm_lut``, ``prefill``, ``unpack_dense``,
+``decode_vmm_noalloc``, ``decode_vmm_accumulate``, ``decode_vmm_lut``, ``prefill``, ``unpack_dense``,
 ``dense_gemm``.
 """
 from __future__ import annotations
@@ -63,6 +63,7 @@ _SIGNATURES = {
     "grinqh_dense_bytes": ([_i64, _i64], _i64),
     "grinqh_unpack_dense": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp], _i32),
     "grinqh_dense_gemm": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
+    "grinqh_decode_vmm_noalloc": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp], _i32),
     "grinqh_decode_vmm_lut": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
 }
 
@@ -238,6 +239,20 @@ def decode_vmm(planes, scales, zeros, x, K: int, N: int, thresholds: Sequence[fl
         planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), x.data_ptr(), K, N, b_max,
         ctypes.cast(th, _vp), ctypes.cast(lv, _vp), n, out.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_vmm_noalloc(planes, scales, zeros, x, K: int, N: int, thresholds: Sequence[float],
+                       levels: Sequence[int], out, stream=None, b_max: int = MAX_BITS):
+    """grinqh_decode_vmm without a workspace: the library's own device array
+    holds the split-K partials (the call allocates nothing; `out` is given)."""
+    import torch
+    _check_layer(planes, scales, zeros, x, K, N, b_max)
+    _dev(out, "y", torch.float32, (N,))
+    th, lv, n = _host_thresholds(thresholds, levels)
+    _check("grinqh_decode_vmm_noalloc", lib().grinqh_decode_vmm_noalloc(
+        planes.data_ptr(), scales.data_ptr(), zeros.data_ptr(), x.data_ptr(), K, N, b_max,
+        ctypes.cast(th, _vp), ctypes.cast(lv, _vp), n, out.data_ptr(), _stream(stream)))
     return out
 
 

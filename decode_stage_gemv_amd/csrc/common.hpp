@@ -101,6 +101,7 @@ int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16
 int launch_vmm_fused_split(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                            const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
                            float* y, float* partials, unsigned* counters, hipStream_t s);
+int noalloc_scratch(int64_t partial_bytes, int64_t tiles, float** partials, unsigned** counters);
 int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                           const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
                           float* y, float* clear, hipStream_t s);

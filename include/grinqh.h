@@ -16,7 +16,8 @@
  * Conventions shared by every call below
  * - Pointers are DEVICE pointers unless the argument says "host".  The caller
  *   allocates and owns every buffer; the library allocates nothing and keeps
- *   no state between calls.
+ *   no state between calls (the one exception is the device array of the
+ *   allocation-free entry point at the end of this header).
  * - fp16 values travel as their IEEE binary16 bit patterns (uint16_t).
  * - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *   enqueues work on it and returns without waiting for the device.
@@ -275,6 +276,27 @@ int grinqh_unpack_dense(const uint8_t* planes, const uint16_t* scales, const uin
  * or a misaligned buffer.
  */
 int grinqh_dense_gemm(const uint16_t* X, const void* dense, int64_t M, int64_t K, int64_t N, float* Y, void* stream);
+
+/*
+ * For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): grinqh_decode_vmm
+ * with no workspace argument.  The split-K partial rows and tile counters
+ * live in a device array inside the library, GRINQH_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from first use until the process ends; this call allocates
+ * nothing.  Every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (two streams, or two graphs replayed at once)
+ * race and must not be issued; calls in stream order are fine.
+ * Arguments, result (bit-identical to grinqh_decode_vmm) and errors as in
+ * grinqh_decode_vmm, plus EINVAL when the layer needs more than the array
+ * holds (more than GRINQH_NOALLOC_SCRATCH_BYTES - 64 KiB of partial rows, or
+ * more than 16384 column tiles; every layer up to 8192 x 28672 and
+ * 28672 x 8192 fits) and EDEVICE when the array's device address cannot be
+ * obtained.
+ */
+#define GRINQH_NOALLOC_SCRATCH_BYTES (16u << 20)
+int grinqh_decode_vmm_noalloc(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
+                              const uint16_t* x, int64_t K, int64_t N, int b_max,
+                              const float* thresholds, const uint8_t* levels, int n, float* y, void* stream);
 
 #ifdef __cplusplus
 }

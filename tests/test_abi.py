@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for name in names:
         assert hasattr(lib, name), name
         assert name in g._SIGNATURES, name
@@ -214,3 +214,22 @@ def test_list_vmm_binding_requires_a_full_length_list():
         grq.vmm(None, None, None, None, None, short, None, K, N, None)
     with pytest.raises(ValueError, match="active_idx"):
         grq.vmm(None, None, None, None, None, [0] * K, None, K, N, None)
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free entry point checks its arguments, and rejects a
+    layer whose split-K partials exceed its fixed device array, before any
+    HIP call (the pointers below are never dereferenced)."""
+    th = (ctypes.c_float * 2)(0.5, 1.0)
+    lv = (ctypes.c_uint8 * 3)(0, 2, 8)
+    p = ctypes.c_void_p(4096)
+    f = lib.grinqh_decode_vmm_noalloc
+    assert f(None, p, p, p, 256, 256, 8, th, lv, 2, p, None) == g.EINVAL
+    assert f(p, p, p, p, 0, 256, 8, th, lv, 2, p, None) == g.EINVAL
+    assert f(p, p, p, p, 256, 256, 9, th, lv, 2, p, None) == g.EINVAL
+    lv_hi = (ctypes.c_uint8 * 3)(0, 2, 8)
+    assert f(p, p, p, p, 256, 256, 4, th, lv_hi, 2, p, None) == g.EINVAL     # level above b_max
+    # 65536 x 65536: 512 row splits x 65536 fp32 partials = 128 MiB > 16 MiB
+    assert f(p, p, p, p, 65536, 65536, 8, th, lv, 2, p, None) == g.EINVAL
+    assert b"allocation-free" in lib.grinqh_last_error()
+    assert g.lib().grinqh_workspace_bytes(65536, 65536) > (16 << 20)
