@@ -110,11 +110,40 @@ def _assign_both(x, th, levels):
 
 @pytest.mark.parametrize("K,cfg,P", [(256, 0, synthetic.P_TINY), (4096, 1, synthetic.P_LEVELS_5[3]),
                                      (14336, 2, synthetic.P_LEVELS_5[2]), (20000, 3, synthetic.P_LEVELS_5[4]),
-                                     (28672, 4, synthetic.P_LEVELS_4[0.5]), (1, 0, synthetic.P_TINY)])
+                                     (28672, 4, synthetic.P_LEVELS_4[0.5]), (1, 0, synthetic.P_TINY),
+                                     (4097, 1, synthetic.P_LEVELS_5[3]), (32773, 3, synthetic.P_LEVELS_5[4]),
+                                     (70001, 2, synthetic.P_LEVELS_5[2]), (4095, 0, synthetic.P_TINY)])
 def test_assign_bit_exact(K, cfg, P):
     levels = synthetic.LEVELS_5 if len(P) == 5 else synthetic.LEVELS_4
     th = oracle.calibrate(synthetic.make_calibration(K, config=cfg, matrix=0), P)
     x = synthetic.make_activations(K, 1, config=cfg, matrix=0)[0]
+    _assign_both(x, th, levels)
+
+
+def test_assign_unaligned_input():
+    """x starting one element past an 8-byte boundary (the per-element path)."""
+    K = 5000
+    th = oracle.calibrate(synthetic.make_calibration(K, config=1, matrix=0), synthetic.P_LEVELS_5[3])
+    x = synthetic.make_activations(K + 1, 1, config=1, matrix=0)[0]
+    full = _dev(x)
+    view = full[1:]
+    assert view.data_ptr() % 8 != 0
+    bits, idx, n = grq.assign_bits(view, th, synthetic.LEVELS_5)
+    torch.cuda.synchronize()
+    b_ref = oracle.assign(x[1:], np.asarray(th, np.float32), synthetic.LEVELS_5)
+    i_ref, n_ref = oracle.compact(b_ref)
+    assert np.array_equal(bits.cpu().numpy(), b_ref)
+    assert int(n.cpu().item()) == n_ref
+    assert np.array_equal(idx.cpu().numpy()[:n_ref], i_ref)
+
+
+@pytest.mark.parametrize("n_th", [0, 1, 2, 3, 5, 6, 7, 8])
+def test_assign_every_threshold_count(n_th):
+    """One kernel per threshold count: each against the oracle."""
+    K = 9000
+    x = synthetic.make_activations(K, 1, config=6, matrix=n_th)[0]
+    th = sorted(float(v) for v in np.random.default_rng(n_th).uniform(0.2, 8.0, size=n_th))
+    levels = tuple(range(n_th + 1)) if n_th < 8 else (0, 1, 2, 3, 4, 5, 6, 7, 8)
     _assign_both(x, th, levels)
 
 
