@@ -73,9 +73,10 @@ int check_assign_params(const float* thresholds, const uint8_t* levels, int n, i
 
 // Workspace geometry used by the VMM kernels and grinqh_workspace_bytes.
 struct VmmGeometry {
-  int64_t rows_per_split;  // K rows handled by one workgroup (64 or 128)
-  int64_t waves;           // waves per workgroup (4 or 8)
-  int64_t splits;          // ceil(K / rows_per_split)
+  int64_t rows_per_split;  // K rows of one sub-item (64 or 128)
+  int64_t subs;            // sub-items per workgroup (1, 2, 4 or 8)
+  int64_t waves;           // waves per workgroup (8 or 16)
+  int64_t splits;          // ceil(K / (rows_per_split subs)): items along K
   int64_t tiles;           // column tiles
   int64_t partial_floats;  // splits * N_pad when splits > 1, else 0
   int64_t counter_offset;  // byte offset of the per-tile counters

@@ -2,16 +2,20 @@
 // "Weight Reconstruction and Bias Correction"; Appendix C.1).
 //
 // Work split.  A workgroup owns one column tile (one row tile of the store
-// per row, ct <= 1024 columns) and one item of 128 (or 64) rows inside one
-// 128-row group of K, so every row it touches shares one (scale, zero) row.
+// per row, ct <= 1024 columns) and S consecutive sub-items of K: a sub-item is
+// 128 (or 64) rows inside one 128-row group, so every row it touches shares
+// one (scale, zero) row.  Large layers use 16-wave workgroups holding S = 2, 4
+// or 8 sub-items (8, 4 or 2 waves each), one workgroup per CU: the sub-items
+// run side by side and the epilogue adds their results, each with its own
+// scale and zero, into one output per column.
 //
-// Row order.  Every wave sees all rows of the group (two per lane) and
+// Row order.  Every wave sees all rows of its sub-item (two per lane) and
 // buckets the active ones by bit width b with ballots, in registers.  Each
 // bucket is cut into "couples" of four rows of one width (the last couple of
 // a bucket is padded with empty rows: x = 0, no bytes).  A couple is two row
 // pairs; the two 32-lane halves of a wave take one pair each, lane l owning
 // 32 columns (one plane word of each row), so the bit width is the same for
-// the whole wave.  Couple k belongs to wave k mod W, W the workgroup's
+// the whole wave.  Couple k belongs to wave k mod W of the sub-item, W its
 // waves (8, 4 or 2; its "records", in order).
 //
 // Loads.  A lane loads its pair's plane words straight into registers with
@@ -48,11 +52,14 @@ namespace grinqh {
 constexpr int kMaxRows = kGroup;                 // rows of one workgroup: 128 or 64, within one scale group
 constexpr int kMaxCouples = kMaxRows / 4 + 6;    // sum over 8 widths of ceil(c_v / 4) <= (128 + 8 * 3) / 4
 constexpr int kRedStride = 33;                   // LDS row stride of the wave reduction
-// Launch shape.  The grid is (row item, column tile) pairs.  Small layers
-// use 64-row items so that more workgroups share the CUs; workgroups have 8
-// waves while two fit per CU, 4 waves up to one round of 16 waves per CU,
-// and 2 waves beyond that, so that the largest layers still run in one
-// round (each wave then takes more records, in a rolled loop).
+// Launch shape.  The grid is (item, column tile) pairs.  Layers with fewer
+// (128-row group, tile) units than CUs use one 8-wave workgroup per 64-row
+// item.  Larger layers use one 16-wave workgroup per item of S = 2, 4 or 8
+// groups (the smallest S that keeps the grid within one workgroup per CU; a
+// sub-item then has 8, 4 or 2 waves, each taking more records, in a rolled
+// loop at 2 waves).  One workgroup per CU instead of several independent ones
+// keeps a CU's loads and arithmetic in one schedule, and the items' output
+// rows are added before they leave the workgroup.
 constexpr int kTargetCUs = 256;                  // MI355X
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;    // buffer offset beyond any range used here
 constexpr int kRsrcWord3 = 0x00020000;           // raw 32-bit buffer, gfx9 family
@@ -66,14 +73,18 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 VmmGeometry vmm_geometry(int64_t K, int64_t N) {
   VmmGeometry g;
   g.tiles = n_tiles(N);
-  g.rows_per_split = n_groups(K) * g.tiles < kTargetCUs ? 64 : 128;
-  g.splits = (K + g.rows_per_split - 1) / g.rows_per_split;
-  // waves per workgroup: 8 while the workgroups fit two per CU, then 4, and
-  // 2 once 4-wave workgroups would need a second round (at four waves per
-  // SIMD a round holds 16 waves per CU): every extra round repeats the
-  // whole latency chain of a workgroup (activations, planes, reduction)
-  const int64_t wgs = g.splits * g.tiles;
-  g.waves = wgs > 4 * kTargetCUs ? 2 : (wgs > 2 * kTargetCUs ? 4 : 8);
+  const int64_t units = n_groups(K) * g.tiles;
+  if (units < kTargetCUs) {
+    g.rows_per_split = 64;
+    g.subs = 1;
+    g.waves = 8;
+  } else {
+    g.rows_per_split = 128;
+    g.subs = units <= 2 * kTargetCUs ? 2 : (units <= 4 * kTargetCUs ? 4 : 8);
+    g.waves = 16;
+  }
+  const int64_t item = g.rows_per_split * g.subs;
+  g.splits = (K + item - 1) / item;
   g.partial_floats = g.splits > 1 ? g.splits * padded_cols(N) : 0;
   g.counter_offset = (g.partial_floats * 4 + 255) / 256 * 256;
   g.bytes = g.splits > 1 ? g.counter_offset + g.tiles * 4 : 0;
@@ -239,35 +250,43 @@ enum : int {
 // scalar registers, so the activation and scale loads issue at once instead
 // of after a fetch of the argument block, and that fetch (thresholds,
 // levels) completes while the activations are in flight.
-template <bool kFused, int kOut, int kWaves>
+template <bool kFused, int kOut, int kWaves, int kSubs>
 __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __restrict__ x,
                                                           const uint8_t* __restrict__ planes,
                                                           const uint16_t* __restrict__ scales,
                                                           const uint16_t* __restrict__ zeros, int K, int N,
                                                           int tiles, int rows, int bmax, VmmArgs a) {
   constexpr int kVmmThreads = 64 * kWaves;
+  constexpr int kSubWaves = kWaves / kSubs;         // waves per sub-item
   constexpr int kCols = kTile / kVmmThreads;        // output columns per thread in the epilogue
-  constexpr int kMaxRecords = (kMaxCouples + kWaves - 1) / kWaves;
+  constexpr int kMaxRecords = (kMaxCouples + kSubWaves - 1) / kSubWaves;
   constexpr int kRedWords = kWaves * 32 * kRedStride;
   __shared__ float s_red[kRedWords];                      // wave reduction
   __shared__ uint32_t s_src[kWaves][kMaxRecords * 4];     // per wave: record row -> source byte offset
   __shared__ uint32_t s_cx[kWaves][kMaxRecords * 2];      // per wave: record pair -> fp16 x of its rows
-  __shared__ float s_hx[2];
+  __shared__ float s_hx[kSubs][2];                        // per sub-item: H and X
+  __shared__ int s_ncp[kSubs];                            // per sub-item: couples (0: no active row)
   __shared__ int s_last;
-  // 2-wave workgroups: each thread has 8 epilogue columns, whose scales and
-  // zeros are parked in LDS during the record loop (registers are short)
-  constexpr bool kParkScales = kWaves == 2;
-  __shared__ uint32_t s_scz[kParkScales ? kTile : 1];
+  // more than two sub-items: each thread's scales and zeros (one pair per
+  // sub-item and column) are parked in LDS during the record loop (registers
+  // are short)
+  constexpr bool kParkScales = kSubs > 2;
+  __shared__ uint32_t s_scz[kParkScales ? kSubs * kTile : 1];
 
-  // workgroup = (column tile, 128-row group), tiles fastest (K, N < 2^31)
+  // workgroup = (column tile, item of kSubs sub-items), tiles fastest (K, N < 2^31)
   const int tile = blockIdx.x % tiles;
   const int split = blockIdx.x / tiles;
-  const int k0 = split * rows;
-  const int k1 = (k0 + rows) < K ? (k0 + rows) : K;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int64_t g = k0 / kGroup;                // scale group
+  const int sub = wid / kSubWaves;              // this wave's sub-item
+  const int swid = wid - sub * kSubWaves;       // the wave's index within it
+  const int kitem = split * rows * kSubs;       // first row of the item
+  // this wave's sub-item: rows [k0, k1), empty past K
+  const int k0 = kitem + sub * rows < K ? kitem + sub * rows : K;
+  const int k1 = (k0 + rows) < K ? (k0 + rows) : K;
+  const int64_t G = (K + kGroup - 1) / kGroup;
+  const int64_t g = k0 / kGroup < G ? k0 / kGroup : G - 1;   // its scale group (clamped when empty)
 
   // ---- every wave sees all rows of the group, two per lane (lane and lane
   // + 64): activation loads first, then scale and zero of this thread's two
@@ -280,7 +299,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int64_t i = k0 + lane + 64 * e;
-      xq[e] = x[i < k1 ? i : k1 - 1];
+      xq[e] = x[i < k1 ? i : (k1 > k0 ? k1 - 1 : K - 1)];
       rq[e] = lane + 64 * e;
     }
   }
@@ -293,15 +312,21 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   const int ct = (Np - t0) < kTile ? (Np - t0) : kTile;   // multiple of 128
   const int pb = ct / 8;                                  // bytes per plane, multiple of 16
   const int rstride = pb * bmax;                          // bytes per row tile
-  uint16_t sc[kCols], zr[kCols];
+  // scale and zero of every sub-item for this thread's epilogue columns
+  uint16_t sc[kSubs][kCols], zr[kSubs][kCols];
 #pragma unroll
-  for (int u = 0; u < kCols; ++u) {
-    int col = tid + u * kVmmThreads;
-    col = col < ct ? col : ct - 1;
-    int gc = t0 + col;
-    gc = gc < N ? gc : N - 1;
-    sc[u] = scales[g * N + gc];
-    zr[u] = zeros[g * N + gc];
+  for (int si = 0; si < kSubs; ++si) {
+    int64_t gs = (int64_t)(kitem + si * rows) / kGroup;
+    gs = gs < G ? gs : G - 1;
+#pragma unroll
+    for (int u = 0; u < kCols; ++u) {
+      int col = tid + u * kVmmThreads;
+      col = col < ct ? col : ct - 1;
+      int gc = t0 + col;
+      gc = gc < N ? gc : N - 1;
+      sc[si][u] = scales[gs * N + gc];
+      zr[si][u] = zeros[gs * N + gc];
+    }
   }
 
   if constexpr (kFused) {
@@ -311,18 +336,18 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   } else {
     // the listed rows of this group: positions [p0, p1) of the list, the
     // two searches in two waves at once (each is a chain of dependent loads)
-    __shared__ int s_p[2];
-    if (wid < 2) {
+    __shared__ int s_p[kSubs][2];
+    if (swid < 2) {
       // a count outside [0, K] (not from a well-formed list) is clamped, so
       // the searches stay inside the K entries the list buffer must hold
       int64_t n = *a.n_active;
       n = n < 0 ? 0 : (n > a.K ? a.K : n);
-      const int64_t p = wave_lower_bound(a.active_idx, n, wid == 0 ? k0 : k1);
-      if (lane == 0) s_p[wid] = (int)p;
+      const int64_t p = wave_lower_bound(a.active_idx, n, swid == 0 ? k0 : k1);
+      if (lane == 0) s_p[sub][swid] = (int)p;
     }
     __syncthreads();
-    const int p0 = s_p[0];
-    int m = s_p[1] - p0;
+    const int p0 = s_p[sub][0];
+    int m = s_p[sub][1] - p0;
     m = m < 0 ? 0 : (m > kMaxRows ? kMaxRows : m);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -356,10 +381,10 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
   for (int v = 1; v <= 8; ++v) cbv[v + 1] = cbv[v] + ((cnt[v] + 3) >> 2);
   const int ncp = cbv[9];
-  const int nrec = ncp > wid ? (ncp - wid + kWaves - 1) / kWaves : 0;   // this wave's couples
+  const int nrec = ncp > swid ? (ncp - swid + kSubWaves - 1) / kSubWaves : 0;   // this wave's couples
 
-  if (wid == kWaves - 1) {
-    // H = sum x phi and X = sum x over the group's active rows (the last
+  if (swid == kSubWaves - 1) {
+    // H = sum x phi and X = sum x over the sub-item's active rows (its last
     // wave has the fewest records, so this stays off the longest path)
     float hs = 0.0f, xs = 0.0f;
 #pragma unroll
@@ -374,8 +399,9 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       xs += __shfl_xor(xs, off, 64);
     }
     if (lane == 0) {
-      s_hx[0] = hs;
-      s_hx[1] = xs;
+      s_hx[sub][0] = hs;
+      s_hx[sub][1] = xs;
+      s_ncp[sub] = ncp;
     }
   }
 
@@ -383,12 +409,12 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   // its own rows that fall into one of them; lanes 0..3 mark padding rows
   uint32_t* const src = s_src[wid];
   uint32_t* const cx = s_cx[wid];
-  // lane j < kMaxRecords describes record j (couple wid + 8 j): its width
+  // lane j < kMaxRecords describes record j (couple swid + W j): its width
   // (0 if the wave has no such record) and, for a width's last couple, the
   // padding places, all in vector registers at once
   int rec_w = 0;
   {
-    const int k = wid + kWaves * lane;
+    const int k = swid + kSubWaves * lane;
     if (lane < kMaxRecords && k < ncp) {
       int v = 1;
 #pragma unroll
@@ -422,8 +448,8 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
         }
       }
       const int k = cb + (rank >> 2);
-      if ((k & (kWaves - 1)) == wid) {
-        const int j = k / kWaves;
+      if ((k & (kSubWaves - 1)) == swid) {
+        const int j = k / kSubWaves;
         src[4 * j + (rank & 3)] = (uint32_t)rq[e] * (uint32_t)rstride;
         reinterpret_cast<uint16_t*>(cx)[4 * j + (rank & 3)] = xq[e];
       }
@@ -438,7 +464,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // buffer descriptor over this group's row tiles of the tile block
+  // buffer descriptor over this sub-item's row tiles of the tile block
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(planes + store_offset((int64_t)t0 * K + (int64_t)k0 * ct, bmax)), (short)0,
       (k1 - k0) * rstride, kRsrcWord3);
@@ -451,12 +477,15 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   if constexpr (kParkScales) {
 #pragma unroll
-    for (int u = 0; u < kCols; ++u) s_scz[tid + u * kVmmThreads] = (uint32_t)sc[u] | ((uint32_t)zr[u] << 16);
+    for (int si = 0; si < kSubs; ++si)
+#pragma unroll
+      for (int u = 0; u < kCols; ++u)
+        s_scz[si * kTile + tid + u * kVmmThreads] = (uint32_t)sc[si][u] | ((uint32_t)zr[si][u] << 16);
   }
   {
     // Three records in flight.  The record sequence is unrolled (8- and
-    // 4-wave workgroups: at most 5 and 10 records a wave) or rolled over
-    // rounds of three (2-wave workgroups) so that the load order is static:
+    // 4-wave sub-items: at most 5 and 10 records a wave) or rolled over
+    // rounds of three (2-wave sub-items) so that the load order is static:
     // record j + 3 is issued into the registers of record j right after j is
     // consumed, and the compiler's wait counts let j + 1 and j + 2 stay
     // outstanding.  Records past nrec load nothing (width 0) and are not
@@ -481,7 +510,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
         }
       }
     } else {
-      // too many records to unroll (2-wave workgroups): a rolled loop over
+      // too many records to unroll (2-wave sub-items): a rolled loop over
       // rounds of three, the three register sets in fixed roles, so that the
       // load order and the wait counts stay static; records past the wave's
       // last load nothing (width 0)
@@ -502,7 +531,6 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   // lane's word, summed over both halves, in half h; then reduce the waves
   // in LDS (row stride 33 keeps both the writes and the column-wise reads
   // free of bank conflicts)
-  const int m = ncp;   // couples (0: no active row)
   float* red = s_red;
   {
     const int hh = lane >> 5;
@@ -511,27 +539,38 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     for (int c = 0; c < 16; ++c) dst[2 * c] = halves_sum(acc[2 * c], acc[2 * c + 1]);
   }
   __syncthreads();
-  const float H = s_hx[0];
-  const float X = s_hx[1];
   // codes entered as c 2^-24 and stand at q 2^(8 - b_max)
   const float afac = __builtin_bit_cast(float, (uint32_t)(127 + 24) << 23);
   const float sfac = __builtin_bit_cast(float, (uint32_t)(127 + bmax - 8) << 23);
+  // sub-items with an active row (the epilogue adds only those)
+  int mall = 0;
+#pragma unroll
+  for (int si = 0; si < kSubs; ++si) mall += s_ncp[si];
+  const int m = mall;
+  // per column: the sum over sub-items of s (A + H) + z X, each sub-item's
+  // A summed over its waves, in wave order
   float val[kCols];
 #pragma unroll
   for (int u = 0; u < kCols; ++u) {
     val[u] = 0.0f;
     const int col = tid + u * kVmmThreads;
-    if (m > 0 && col < ct && t0 + col < N) {
-      float A = 0.0f;
+    if (col < ct && t0 + col < N) {
 #pragma unroll
-      for (int h = 0; h < kWaves; ++h) A += red[(h * 32 + (col >> 5)) * kRedStride + (col & 31)];
-      uint16_t su = sc[u], zu = zr[u];
-      if constexpr (kParkScales) {
-        const uint32_t p = s_scz[col];
-        su = (uint16_t)(p & 0xFFFFu);
-        zu = (uint16_t)(p >> 16);
+      for (int si = 0; si < kSubs; ++si) {
+        if (s_ncp[si] > 0) {
+          float A = 0.0f;
+#pragma unroll
+          for (int h = 0; h < kSubWaves; ++h)
+            A += red[((si * kSubWaves + h) * 32 + (col >> 5)) * kRedStride + (col & 31)];
+          uint16_t su = sc[si][u], zu = zr[si][u];
+          if constexpr (kParkScales) {
+            const uint32_t p = s_scz[si * kTile + col];
+            su = (uint16_t)(p & 0xFFFFu);
+            zu = (uint16_t)(p >> 16);
+          }
+          val[u] += (half_bits_to_float(su) * sfac) * (A * afac + s_hx[si][0]) + half_bits_to_float(zu) * s_hx[si][1];
+        }
       }
-      val[u] = (half_bits_to_float(su) * sfac) * (A * afac + H) + half_bits_to_float(zu) * X;
     }
   }
 
@@ -595,36 +634,38 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     }
     __syncthreads();
     if (!s_last) return;
+    // thread t < 256 adds columns 4t .. 4t + 3 with 16-byte loads (the
+    // partial rows are 16-byte aligned: N_pad is a multiple of 128), kRound
+    // splits per round with all loads of a round in flight together; splits
+    // past the end and columns past the tile read as zero (out-of-range
+    // offsets); the sum runs in split order
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.partials + t0), (short)0, (int)(a.splits * Np * 4), (int)kRsrcWord3);
     const uint32_t row_bytes = (uint32_t)(Np * 4);
-    float sum[kCols];
+    if (tid < kTile / 4) {
+      const int c4 = 4 * tid;
+      float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      constexpr int kRound = 16;
+      for (int sp0 = 0; sp0 < a.splits; sp0 += kRound) {
+        uint32_t v[kRound][4];
 #pragma unroll
-    for (int e = 0; e < kCols; ++e) sum[e] = 0.0f;
-    constexpr int kRound = 64 / kCols;   // splits per round (loads in flight per thread: 64)
-    // kRound splits per round, all loads of a round in flight together;
-    // splits past the end read as zero (out-of-range offsets); the sum runs
-    // in split order
-    for (int sp0 = 0; sp0 < a.splits; sp0 += kRound) {
-      uint32_t v[kRound][kCols];
-#pragma unroll
-      for (int u = 0; u < kRound; ++u)
-#pragma unroll
-        for (int e = 0; e < kCols; ++e) {
-          const int col = tid + e * kVmmThreads;
-          const bool ok = sp0 + u < a.splits && col < ct;
-          const uint32_t off = ok ? (uint32_t)(sp0 + u) * row_bytes + 4u * (uint32_t)col : kOutOfRange;
-          v[u][e] = __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, kScopeDevice);
+        for (int u = 0; u < kRound; ++u) {
+          const bool ok = sp0 + u < a.splits && c4 < ct;
+          const uint32_t off = ok ? (uint32_t)(sp0 + u) * row_bytes + 4u * (uint32_t)c4 : kOutOfRange;
+          const auto q = __builtin_amdgcn_raw_buffer_load_b128(prs, (int)off, 0, kScopeDevice);
+          v[u][0] = q[0];
+          v[u][1] = q[1];
+          v[u][2] = q[2];
+          v[u][3] = q[3];
         }
 #pragma unroll
-      for (int u = 0; u < kRound; ++u)
+        for (int u = 0; u < kRound; ++u)
 #pragma unroll
-        for (int e = 0; e < kCols; ++e) sum[e] += __builtin_bit_cast(float, v[u][e]);
-    }
+          for (int e = 0; e < 4; ++e) sum[e] += __builtin_bit_cast(float, v[u][e]);
+      }
 #pragma unroll
-    for (int e = 0; e < kCols; ++e) {
-      const int col = tid + e * kVmmThreads;
-      if (col < ct && t0 + col < N) a.y[t0 + col] = sum[e];
+      for (int e = 0; e < 4; ++e)
+        if (c4 + e < ct && t0 + c4 + e < N) a.y[t0 + c4 + e] = sum[e];
     }
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -637,12 +678,12 @@ static unsigned* ws_counters(void* ws, int64_t K, int64_t N) {
   return g.bytes > 0 && ws ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + g.counter_offset) : nullptr;
 }
 
-template <int kWaves>
+template <int kWaves, int kSubs>
 static void launch_shape(bool fused, int out_mode, dim3 grid, const VmmArgs& a, hipStream_t s) {
   const dim3 block(64 * kWaves);
-#define GRINQH_VMM_LAUNCH(F, O)                                                                              \
-  hipLaunchKernelGGL((vmm_kernel<F, O, kWaves>), grid, block, 0, s, a.x, a.planes, a.scales, a.zeros, (int)a.K, \
-                     (int)a.N, a.tiles, a.rows, a.bmax, a)
+#define GRINQH_VMM_LAUNCH(F, O)                                                                          \
+  hipLaunchKernelGGL((vmm_kernel<F, O, kWaves, kSubs>), grid, block, 0, s, a.x, a.planes, a.scales, a.zeros, \
+                     (int)a.K, (int)a.N, a.tiles, a.rows, a.bmax, a)
   if (out_mode == kOutAccumulate) {
     if (fused)
       GRINQH_VMM_LAUNCH(true, kOutAccumulate);
@@ -671,12 +712,14 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, float* partials, uns
   a.partials = partials;
   a.counters = counters;
   const dim3 grid((unsigned)(g.splits * g.tiles));
-  if (g.waves == 2)
-    launch_shape<2>(fused, out_mode, grid, a, s);
-  else if (g.waves == 4)
-    launch_shape<4>(fused, out_mode, grid, a, s);
+  if (g.subs == 8)
+    launch_shape<16, 8>(fused, out_mode, grid, a, s);
+  else if (g.subs == 4)
+    launch_shape<16, 4>(fused, out_mode, grid, a, s);
+  else if (g.subs == 2)
+    launch_shape<16, 2>(fused, out_mode, grid, a, s);
   else
-    launch_shape<8>(fused, out_mode, grid, a, s);
+    launch_shape<8, 1>(fused, out_mode, grid, a, s);
   return check_launch(out_mode == kOutAccumulate ? "grinqh_decode_vmm_accumulate"
                                                  : (fused ? "grinqh_decode_vmm" : "grinqh_vmm"));
 }
