@@ -137,6 +137,60 @@ def test_assign_unaligned_input():
     assert np.array_equal(idx.cpu().numpy()[:n_ref], i_ref)
 
 
+@pytest.mark.parametrize("offset", [1, 4, 8])
+def test_assign_misaligned_views(offset):
+    """x 2-, 8- and 16-byte aligned views (below 16 the element-wise loads);
+    with the 16-byte aligned x, bits starts 3 bytes past an 8-byte boundary."""
+    K = 9001
+    th = oracle.calibrate(synthetic.make_calibration(K, config=1, matrix=1), synthetic.P_LEVELS_5[3])
+    x = synthetic.make_activations(K + offset, 1, config=1, matrix=1)[0]
+    view = _dev(x)[offset:]
+    bits_out = torch.empty(K + 3, dtype=torch.uint8, device="cuda")[3:] if offset == 8 else None
+    bits, idx, n = grq.assign_bits(view, th, synthetic.LEVELS_5, bits=bits_out)
+    torch.cuda.synchronize()
+    b_ref = oracle.assign(x[offset:], np.asarray(th, np.float32), synthetic.LEVELS_5)
+    i_ref, n_ref = oracle.compact(b_ref)
+    assert np.array_equal(bits.cpu().numpy(), b_ref)
+    assert int(n.cpu().item()) == n_ref
+    assert np.array_equal(idx.cpu().numpy()[:n_ref], i_ref)
+
+
+@pytest.mark.parametrize("K,offset", [(131072, 0), (131073, 0), (200003, 0), (140001, 1)])
+def test_assign_long_inputs(K, offset):
+    """The largest chunked input (64 chunks) and the single-workgroup path past it."""
+    th = oracle.calibrate(synthetic.make_calibration(K, config=2, matrix=0), synthetic.P_LEVELS_5[2])
+    x = synthetic.make_activations(K + offset, 1, config=2, matrix=0)[0]
+    view = _dev(x)[offset:]
+    bits, idx, n = grq.assign_bits(view, th, synthetic.LEVELS_5)
+    torch.cuda.synchronize()
+    b_ref = oracle.assign(x[offset:], np.asarray(th, np.float32), synthetic.LEVELS_5)
+    i_ref, n_ref = oracle.compact(b_ref)
+    assert np.array_equal(bits.cpu().numpy(), b_ref)
+    assert int(n.cpu().item()) == n_ref
+    assert np.array_equal(idx.cpu().numpy()[:n_ref], i_ref)
+
+
+def test_assign_special_values_in_every_chunk():
+    """NaN, infinities, signed zeros, subnormals and exact threshold ties spread
+    over several 2048-row chunks, under level tables whose active rows are not
+    one interval of |x|: each chunk's count of the rows before it must agree
+    with the widths of those rows."""
+    K = 11000
+    rng = np.random.default_rng(7)
+    x = synthetic.make_activations(K, 1, config=7, matrix=1)[0].copy()
+    specials = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 6e-8, -6e-8, 0.5, -1.0, 2.0, -4.0, 65504.0,
+                         -np.nan, 1.0009765625], np.float16)
+    pos = rng.choice(K, size=700, replace=False)
+    x[pos] = specials[rng.integers(0, len(specials), size=pos.size)]
+    th = [0.5, 1.0, 2.0, 4.0]
+    for lv in [(0, 2, 3, 4, 8), (2, 0, 8, 0, 3), (0, 3, 0, 5, 0), (1, 1, 1, 1, 1), (0, 0, 0, 0, 0),
+               (5, 0, 0, 0, 0), (0, 0, 0, 0, 7), (4, 4, 0, 4, 4)]:
+        _assign_both(x, th, lv)
+    _assign_both(x, [0.0, 0.5, 0.5, 65504.0, float("inf")], (0, 1, 0, 2, 0, 3))
+    _assign_both(x, [0.0, 0.5, 0.5, 65504.0, float("inf")], (3, 1, 0, 2, 0, 0))
+    _assign_both(x, [6e-8, 1e-5, 0.25, 0.75, 1.5, 3.0, 70000.0, float("inf")], (0, 1, 0, 1, 0, 1, 0, 1, 0))
+
+
 @pytest.mark.parametrize("n_th", [0, 1, 2, 3, 5, 6, 7, 8])
 def test_assign_every_threshold_count(n_th):
     """One kernel per threshold count: each against the oracle."""
