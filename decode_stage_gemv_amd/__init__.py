@@ -26,7 +26,7 @@ TILE = 1024
 MAX_THRESHOLDS = 8
 MAX_BITS = 8
 
-OK, EINVAL, EDEVICE = 0, -1, -2
+OK, EINVAL, EDEVICE, ENOSYS = 0, -1, -2, -3
 
 
 class GrinqhError(RuntimeError):

@@ -95,6 +95,7 @@ const char* grinqh_status_string(int status) {
     case GRINQH_OK: return "ok";
     case GRINQH_EINVAL: return "invalid argument";
     case GRINQH_EDEVICE: return "device error";
+    case GRINQH_ENOSYS: return "not implemented";
     default: return "unknown status";
   }
 }

@@ -59,7 +59,9 @@ extern "C" {
 enum {
     GRINQH_OK = 0,
     GRINQH_EINVAL = -1,   /* bad argument; nothing was enqueued */
-    GRINQH_EDEVICE = -2   /* HIP reported an error (no device, launch failure) */
+    GRINQH_EDEVICE = -2,  /* HIP reported an error (no device, launch failure) */
+    GRINQH_ENOSYS = -3    /* reserved for an entry point without an implementation;
+                             every call declared here is implemented, so none returns it */
 };
 
 #define GRINQH_GROUP 128          /* rows per (scale, zero) group */

@@ -38,6 +38,8 @@ def test_static_queries(lib):
     assert lib.grinqh_status_string(0) == b"ok"
     assert lib.grinqh_status_string(-1) == b"invalid argument"
     assert lib.grinqh_status_string(-2) == b"device error"
+    assert lib.grinqh_status_string(-3) == b"not implemented"
+    assert lib.grinqh_status_string(7) == b"unknown status"
     assert lib.grinqh_planes_bytes(4096, 14336, 8) == 4096 * 14336
     assert lib.grinqh_planes_bytes(4096, 14336, 6) == 4096 * 14336 * 6 // 8
     assert lib.grinqh_planes_bytes(4096, 14336, 4) == 4096 * 14336 // 2
