@@ -7,7 +7,9 @@
 // one (scale, zero) row.  Large layers use 16-wave workgroups holding S = 2, 4
 // or 8 sub-items (8, 4 or 2 waves each), one workgroup per CU: the sub-items
 // run side by side and the epilogue adds their results, each with its own
-// scale and zero, into one output per column.
+// scale and zero, into one output per column.  Where that would leave CUs
+// idle, 4-wave workgroups of one 128-row sub-item share the CUs, and small
+// layers use 8-wave workgroups of one 64-row sub-item (choose_shape).
 //
 // Row order.  Every wave sees all rows of its sub-item (two per lane) and
 // buckets the active ones by bit width b with ballots, in registers.  Each
@@ -52,14 +54,15 @@ namespace grinqh {
 constexpr int kMaxRows = kGroup;                 // rows of one workgroup: 128 or 64, within one scale group
 constexpr int kMaxCouples = kMaxRows / 4 + 6;    // sum over 8 widths of ceil(c_v / 4) <= (128 + 8 * 3) / 4
 constexpr int kRedStride = 33;                   // LDS row stride of the wave reduction
-// Launch shape.  The grid is (item, column tile) pairs.  Layers with fewer
-// (128-row group, tile) units than CUs use one 8-wave workgroup per 64-row
-// item.  Larger layers use one 16-wave workgroup per item of S = 2, 4 or 8
-// groups (the smallest S that keeps the grid within one workgroup per CU; a
-// sub-item then has 8, 4 or 2 waves, each taking more records, in a rolled
-// loop at 2 waves).  One workgroup per CU instead of several independent ones
-// keeps a CU's loads and arithmetic in one schedule, and the items' output
-// rows are added before they leave the workgroup.
+// Launch shape.  The grid is (item, column tile) pairs; an item is S
+// sub-items of R rows (R = 128, or 64 on small layers).  The shapes are
+// 16-wave workgroups with S = 1, 2, 4 or 8 (a sub-item then has 16, 8, 4 or
+// 2 waves, each taking more records, in a rolled loop at 2 waves), 4-wave
+// workgroups with one 128-row sub-item (several per CU, for layers whose
+// 16-wave grid would leave CUs idle), and 8-wave workgroups with one 64-row
+// sub-item (small layers); choose_shape picks one per layer.  One workgroup
+// per CU keeps a CU's loads and arithmetic in one schedule, and the
+// sub-items' output rows are added before they leave the workgroup.
 constexpr int kTargetCUs = 256;                  // MI355X
 constexpr uint32_t kOutOfRange = 0x7FFFFF00u;    // buffer offset beyond any range used here
 constexpr int kRsrcWord3 = 0x00020000;           // raw 32-bit buffer, gfx9 family
@@ -70,19 +73,44 @@ constexpr int kWaitVm0 = 0x0F70;                 // vmcnt(0) only
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+// The shape of one workgroup: waves, sub-items and rows per sub-item.
+struct VmmShape {
+  int waves, subs, rows;
+};
+
+// Pick the workgroup shape whose busiest CU holds the fewest rows, among
+// shapes whose whole grid is resident at once (at most 16 waves per CU, the
+// kernels' occupancy); ties go to the larger workgroup (one schedule per
+// CU).  Measured per layer on MI355X: 128-row sub-items beat 64-row ones
+// except on small layers, where a 64-row item doubles the workgroups.  The
+// set of shapes is kept small on purpose: a decode pass alternates layers,
+// and each kernel is tens of KB of code, so layers that share a kernel find
+// its code still in the instruction cache.
+static VmmShape choose_shape(int64_t K, int64_t N) {
+  static const VmmShape kShapes[] = {{16, 2, 128}, {16, 4, 128}, {16, 8, 128}, {4, 1, 128}, {8, 1, 64}};
+  const int64_t tiles = n_tiles(N);
+  VmmShape best = {16, 8, 128};   // layers too large for one round
+  int64_t best_rows = -1;
+  for (const VmmShape& c : kShapes) {
+    const int64_t wgs = (K + (int64_t)c.rows * c.subs - 1) / ((int64_t)c.rows * c.subs) * tiles;
+    const int64_t per_cu = (wgs + kTargetCUs - 1) / kTargetCUs;
+    if (per_cu * c.waves > 16) continue;
+    const int64_t rows = per_cu * c.subs * c.rows;
+    if (best_rows < 0 || rows < best_rows || (rows == best_rows && c.waves > best.waves)) {
+      best = c;
+      best_rows = rows;
+    }
+  }
+  return best;
+}
+
 VmmGeometry vmm_geometry(int64_t K, int64_t N) {
   VmmGeometry g;
   g.tiles = n_tiles(N);
-  const int64_t units = n_groups(K) * g.tiles;
-  if (units < kTargetCUs) {
-    g.rows_per_split = 64;
-    g.subs = 1;
-    g.waves = 8;
-  } else {
-    g.rows_per_split = 128;
-    g.subs = units <= 2 * kTargetCUs ? 2 : (units <= 4 * kTargetCUs ? 4 : 8);
-    g.waves = 16;
-  }
+  const VmmShape sh = choose_shape(K, N);
+  g.rows_per_split = sh.rows;
+  g.subs = sh.subs;
+  g.waves = sh.waves;
   const int64_t item = g.rows_per_split * g.subs;
   g.splits = (K + item - 1) / item;
   g.partial_floats = g.splits > 1 ? g.splits * padded_cols(N) : 0;
@@ -483,9 +511,10 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
         s_scz[si * kTile + tid + u * kVmmThreads] = (uint32_t)sc[si][u] | ((uint32_t)zr[si][u] << 16);
   }
   {
-    // Three records in flight.  The record sequence is unrolled (8- and
-    // 4-wave sub-items: at most 5 and 10 records a wave) or rolled over
-    // rounds of three (2-wave sub-items) so that the load order is static:
+    // Three records in flight.  The record sequence is unrolled (8-wave
+    // sub-items: at most 5 records a wave) or rolled over rounds of three
+    // (sub-items of 4 or 2 waves: up to 10 or 19 records) so that the load
+    // order is static:
     // record j + 3 is issued into the registers of record j right after j is
     // consumed, and the compiler's wait counts let j + 1 and j + 2 stay
     // outstanding.  Records past nrec load nothing (width 0) and are not
@@ -500,7 +529,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       bw[j] = width(j);
       load_record<kMaxRecords>(rr[j], rsrc, src, j, bw[j], pb, lane_off);
     }
-    if constexpr (kMaxRecords <= 12) {
+    if constexpr (kMaxRecords <= 5) {
 #pragma unroll
       for (int j = 0; j < kMaxRecords; ++j) {
         if (j < nrec) compute_record(rr[j % 3], bw[j % 3], cx[2 * j + h], acc);
@@ -510,10 +539,12 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
         }
       }
     } else {
-      // too many records to unroll (2-wave sub-items): a rolled loop over
-      // rounds of three, the three register sets in fixed roles, so that the
-      // load order and the wait counts stay static; records past the wave's
-      // last load nothing (width 0)
+      // a rolled loop over rounds of three, the three register sets in fixed
+      // roles, so that the load order and the wait counts stay static;
+      // records past the wave's last load nothing (width 0).  Unrolled, each
+      // record slot is a copy of the rebuild for every width (about 5 KB of
+      // code): ten slots made a 55 KB kernel whose instruction fetches cost
+      // more than the loop when layers alternate
       for (int j0 = 0; j0 < nrec; j0 += 3) {
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
@@ -712,14 +743,15 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, float* partials, uns
   a.partials = partials;
   a.counters = counters;
   const dim3 grid((unsigned)(g.splits * g.tiles));
-  if (g.subs == 8)
-    launch_shape<16, 8>(fused, out_mode, grid, a, s);
-  else if (g.subs == 4)
-    launch_shape<16, 4>(fused, out_mode, grid, a, s);
-  else if (g.subs == 2)
-    launch_shape<16, 2>(fused, out_mode, grid, a, s);
-  else
-    launch_shape<8, 1>(fused, out_mode, grid, a, s);
+  const int shape = (int)(g.waves * 16 + g.subs);
+  switch (shape) {
+    case 16 * 16 + 8: launch_shape<16, 8>(fused, out_mode, grid, a, s); break;
+    case 16 * 16 + 4: launch_shape<16, 4>(fused, out_mode, grid, a, s); break;
+    case 16 * 16 + 2: launch_shape<16, 2>(fused, out_mode, grid, a, s); break;
+    case 8 * 16 + 1: launch_shape<8, 1>(fused, out_mode, grid, a, s); break;
+    case 4 * 16 + 1: launch_shape<4, 1>(fused, out_mode, grid, a, s); break;
+    default: return fail(GRINQH_EINVAL, "no kernel for %lld waves x %lld sub-items", (long long)g.waves, (long long)g.subs);
+  }
   return check_launch(out_mode == kOutAccumulate ? "grinqh_decode_vmm_accumulate"
                                                  : (fused ? "grinqh_decode_vmm" : "grinqh_vmm"));
 }

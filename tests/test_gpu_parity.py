@@ -406,3 +406,39 @@ def test_decode_vmm_accumulate_ping_pong():
         _check_y(bufs[step % 2].cpu().numpy(), lay.codes, lay.scales, lay.zeros, x,
                  oracle.assign(x, th, synthetic.LEVELS_5))
         assert torch.count_nonzero(bufs[(step + 1) % 2]).item() == 0
+
+
+# ------------------------------------------------------- every workgroup shape
+
+# Layers whose shapes select each less common workgroup shape of the VMM
+# (waves x sub-items x rows): 8 x 1 x 64 with two workgroups per CU (a few
+# hundred 128-row units), 4 x 1 x 128 (several small workgroups per CU, the
+# rolled record loop), 16 x 4 x 128 (one 512-row item per CU), exact and
+# ragged in K and N.
+SHAPE_CASES = [
+    (2048, 9216, 2, 5, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5),
+    (2100, 9000, 5, 6, synthetic.P_LEVELS_5[2], synthetic.LEVELS_5),
+    (4096, 24576, 2, 6, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5),
+    (4000, 24000, 5, 7, synthetic.P_LEVELS_5[4], synthetic.LEVELS_5),
+    (8192, 16384, 2, 7, synthetic.P_LEVELS_5[3], synthetic.LEVELS_5),
+    (8000, 16000, 5, 8, synthetic.P_LEVELS_4[1], synthetic.LEVELS_4),
+]
+
+
+@pytest.mark.parametrize("K,N,cfg,mat,P,levels", SHAPE_CASES)
+def test_every_workgroup_shape(K, N, cfg, mat, P, levels):
+    """All three entry points (split-K fused, list, accumulate) on every
+    column, against the oracle; the split-K and list results bit-identical."""
+    lay = synthetic.make_layer(K, N, config=cfg, matrix=mat, n_test=1)
+    th = oracle.calibrate(lay.calib, P)
+    x = lay.x[0]
+    y, planes, ws = _run_decode(lay, x, th, levels)
+    bits = oracle.assign(x, th, levels)
+    _check_y(y, lay.codes, lay.scales, lay.zeros, x, bits)
+    b, idx, n = grq.assign_bits(_dev(x), th, levels)
+    y2 = grq.vmm(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), b, idx, n, K, N, ws)
+    acc = torch.zeros(N, dtype=torch.float32, device="cuda")
+    grq.decode_vmm_accumulate(planes, _dev(lay.scales), _dev(lay.zeros), _dev(x), K, N, th, levels, acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(y2.cpu().numpy().view(np.uint32), y.view(np.uint32))
+    _check_y(acc.cpu().numpy(), lay.codes, lay.scales, lay.zeros, x, bits)
