@@ -323,7 +323,11 @@ class Stack:
     bits over levels {0,2,3,4,8}.
 
     fused=False: one VMM per matrix, each with its own activation and
-    thresholds (252 launches per token).  fused=True: the matrices that read
+    thresholds (252 launches per token).  grouped=True: the same per-matrix
+    VMMs, with the matrices that sit at one position of the layer (q, k and
+    v; gate and up) issued as one grouped launch (144 launches per token;
+    every matrix keeps its own store, activation and thresholds, and the
+    launches keep the layer order).  fused=True: the matrices that read
     the same input in the model are packed side by side by columns, q|k|v
     and gate|up, and share one activation and one set of thresholds (the
     thresholds depend only on the input's calibration vectors), so a layer
@@ -334,15 +338,28 @@ class Stack:
 
     GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
-    def __init__(self, keep_cols=0, fused=False, progress=True):
+    def __init__(self, keep_cols=0, fused=False, progress=True, grouped=False):
         import torch
         import synthetic
         import decode_stage_gemv_amd as grq
         t0 = time.time()
         dev = torch.device("cuda:0")
+        if fused and grouped:
+            raise ValueError("the fused stack has no separate matrices to group")
         self.fused = fused
         self.P, self.levels = synthetic.P_LEVELS_5[3], synthetic.LEVELS_5
         listing = synthetic.qwen3_stack()
+        # launch groups: positions in self.mats issued together
+        self.groups = None
+        if grouped:
+            gid = {name: g for g, grp in enumerate(self.GROUPS) for name in grp}
+            self.groups = []
+            for j, (_, layer, name, _, _) in enumerate(listing):
+                if self.groups and self.groups[-1][0] == (layer, gid[name]):
+                    self.groups[-1][1].append(j)
+                else:
+                    self.groups.append(((layer, gid[name]), [j]))
+            self.groups = [g for _, g in self.groups]
         if fused:
             by = {(layer, name): (idx, K, N) for idx, layer, name, K, N in listing}
             units = [[(by[(layer, n)][0], n) + by[(layer, n)][1:] for n in grp]
@@ -377,14 +394,26 @@ class Stack:
         self.ys = [[torch.zeros(m["N"], dtype=torch.float32, device=dev) for m in self.mats] for _ in range(2)]
         self.plane_bytes = sum(m["planes"].numel() for m in self.mats)
         torch.cuda.synchronize()
-        log(f"stack{' (fused projections)' if fused else ''}: {len(self.mats)} VMMs per token, "
+        log(f"stack{' (fused projections)' if fused else (' (grouped launches)' if grouped else '')}: "
+            f"{len(self.mats)} VMMs in {self.launches} launches per token, "
             f"{self.plane_bytes / 1e9:.2f} GB of planes resident, setup {time.time() - t0:.1f}s")
+
+    @property
+    def launches(self):
+        return len(self.groups) if self.groups is not None else len(self.mats)
 
     def token(self, t):
         """One token's VMMs (decode-loop form: add into output set t % 2,
         clear set (t + 1) % 2 for the next token)."""
         import decode_stage_gemv_amd as grq
         ya, yb = self.ys[t % 2], self.ys[(t + 1) % 2]
+        if self.groups is not None:
+            for grp in self.groups:
+                ms = [self.mats[j] for j in grp]
+                grq.decode_vmm_accumulate_group(
+                    [(m["planes"], m["scales"], m["zeros"], m["x"], m["N"], m["thresholds"], self.levels,
+                      ya[j], yb[j]) for j, m in zip(grp, ms)], ms[0]["K"])
+            return
         for j, m in enumerate(self.mats):
             grq.decode_vmm_accumulate(m["planes"], m["scales"], m["zeros"], m["x"], m["K"], m["N"],
                                       m["thresholds"], self.levels, ya[j], yb[j])
@@ -400,11 +429,11 @@ class Stack:
         return total, bits / sum(m["K"] * m["N"] for m in self.mats)
 
 
-def stack_bench(fused=False, tokens=4, warmup=2):
+def stack_bench(fused=False, tokens=4, warmup=2, grouped=False):
     """Time per token of the Qwen3-8B stack: `tokens` passes captured in one
     HIP graph, timed over one replay with events on the capture stream."""
     import torch
-    st = Stack(fused=fused)
+    st = Stack(fused=fused, grouped=grouped)
     nbytes, avg_bits = st.bytes_per_token()
     for t in range(warmup):
         st.token(t)
@@ -427,13 +456,17 @@ def stack_bench(fused=False, tokens=4, warmup=2):
     us = start.elapsed_time(stop) * 1e3 / tokens
     gbs = nbytes / (us * 1e-6) / 1e9
     n = len(st.mats)
-    out = {"model": "qwen3-8b linear stack (36 layers x q,k,v,o,gate,up,down)",
-           "form": ("fused projections: q|k|v and gate|up packed side by side, sharing x and thresholds"
-                    if fused else "one VMM per matrix, fresh x per VMM"),
-           "vmms_per_token": n, "entry_point": ENTRY["accumulate"], "avg_bits": avg_bits,
+    form = ("fused projections: q|k|v and gate|up packed side by side, sharing x and thresholds" if fused else
+            ("one VMM per matrix, fresh x per VMM; q,k,v and gate,up of a layer in one grouped launch each"
+             if grouped else "one VMM per matrix, fresh x per VMM"))
+    out = {"model": "qwen3-8b linear stack (36 layers x q,k,v,o,gate,up,down)", "form": form,
+           "vmms_per_token": n, "launches_per_token": st.launches,
+           "entry_point": "grinqh_decode_vmm_accumulate_group" if grouped else ENTRY["accumulate"],
+           "avg_bits": avg_bits,
            "plane_bytes_resident": st.plane_bytes, "bytes_per_token": nbytes, "us_per_token": us,
            "us_per_vmm": us / n, "GB_s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "tokens_timed": tokens}
-    log(f"stack{' fused' if fused else ''}: {us:.1f} us per token ({us / n:.2f} us per VMM, {n} VMMs), "
+    log(f"stack{' fused' if fused else (' grouped' if grouped else '')}: {us:.1f} us per token "
+        f"({us / n:.2f} us per VMM, {n} VMMs, {st.launches} launches), "
         f"{nbytes / 1e9:.3f} GB per token, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak), "
         f"avg bits {avg_bits:.3f}")
     del st, g
@@ -689,7 +722,8 @@ def main():
         print(json.dumps({"copy_probe": copy_probe()}), flush=True)
         return
     if args.stack_only:
-        print(json.dumps({"stack": stack_bench(), "stack_fused": stack_bench(fused=True)}), flush=True)
+        print(json.dumps({"stack": stack_bench(), "stack_grouped": stack_bench(grouped=True),
+                          "stack_fused": stack_bench(fused=True)}), flush=True)
         return
     if args.lut_only:
         print(json.dumps({"lut": lut_bench(args.workload, min(args.steps, 100), min(args.warmup, 10))}), flush=True)
@@ -783,9 +817,10 @@ def main():
     if not args.no_lut and not args.only:
         lut = lut_bench(args.workload, min(args.steps, 100), min(args.warmup, 10))
 
-    stack = stack_fused = None
+    stack = stack_grouped = stack_fused = None
     if not args.no_stack and not args.only:
         stack = stack_bench()
+        stack_grouped = stack_bench(grouped=True)
         stack_fused = stack_bench(fused=True)
 
     copy = copy_probe()
@@ -832,6 +867,7 @@ def main():
         out["lut"] = lut
     if stack:
         out["stack"] = stack
+        out["stack_grouped"] = stack_grouped
         out["stack_fused"] = stack_fused
     print(json.dumps(out), flush=True)
 

@@ -58,6 +58,8 @@ _SIGNATURES = {
     "grinqh_decode_vmm": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _sz, _vp], _i32),
     "grinqh_decode_vmm_accumulate": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp],
                                      _i32),
+    "grinqh_decode_vmm_accumulate_group": ([_i32, _vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp,
+                                            _vp], _i32),
     "grinqh_prefill": ([_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp], _i32),
     "grinqh_lut_entries": ([_i64, _i32], _i64),
     "grinqh_dense_bytes": ([_i64, _i64], _i64),
@@ -270,6 +272,39 @@ def decode_vmm_accumulate(planes, scales, zeros, x, K: int, N: int, thresholds: 
         ctypes.cast(th, _vp), ctypes.cast(lv, _vp), n, y.data_ptr(),
         clear.data_ptr() if clear is not None else None, _stream(stream)))
     return y
+
+
+MAX_GROUP = 4
+
+
+def decode_vmm_accumulate_group(members, K: int, stream=None, b_max: int = MAX_BITS):
+    """Several independent accumulating decode steps in one launch.
+
+    members: up to MAX_GROUP tuples (planes, scales, zeros, x, N, thresholds,
+    levels, y, clear) with clear None or a buffer to zero; every member's y
+    gets += x W of its own layer (K rows each).
+    """
+    import torch
+    count = len(members)
+    if not 1 <= count <= MAX_GROUP:
+        raise ValueError(f"{count} members, expected 1..{MAX_GROUP}")
+    arr = lambda vals: (ctypes.c_void_p * count)(*vals)
+    keep = []   # host threshold and level arrays must outlive the call
+    for (planes, scales, zeros, x, N, thresholds, levels, y, clear) in members:
+        _check_layer(planes, scales, zeros, x, K, N, b_max)
+        _dev(y, "y", torch.float32, (N,))
+        if clear is not None:
+            _dev(clear, "clear", torch.float32, (N,))
+        keep.append(_host_thresholds(thresholds, levels))
+    Ns = (ctypes.c_int64 * count)(*[int(m[4]) for m in members])
+    ns = (ctypes.c_int * count)(*[k[2] for k in keep])
+    _check("grinqh_decode_vmm_accumulate_group", lib().grinqh_decode_vmm_accumulate_group(
+        count, arr([m[0].data_ptr() for m in members]), arr([m[1].data_ptr() for m in members]),
+        arr([m[2].data_ptr() for m in members]), arr([m[3].data_ptr() for m in members]), K, Ns, b_max,
+        arr([ctypes.cast(k[0], _vp).value for k in keep]), arr([ctypes.cast(k[1], _vp).value for k in keep]), ns,
+        arr([m[7].data_ptr() for m in members]),
+        arr([m[8].data_ptr() if m[8] is not None else None for m in members]), _stream(stream)))
+    return [m[7] for m in members]
 
 
 def prefill(planes, scales, zeros, X, K: int, N: int, out=None, stream=None, b_max: int = MAX_BITS):

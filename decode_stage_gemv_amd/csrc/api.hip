@@ -202,6 +202,44 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
   return launch_vmm_accumulate(planes, scales, zeros, x, K, N, b_max, ap, y, clear, as_stream(stream));
 }
 
+int grinqh_decode_vmm_accumulate_group(int count, const uint8_t* const* planes, const uint16_t* const* scales,
+                                       const uint16_t* const* zeros, const uint16_t* const* x, int64_t K,
+                                       const int64_t* N, int b_max, const float* const* thresholds,
+                                       const uint8_t* const* levels, const int* n, float* const* y,
+                                       float* const* clear, void* stream) {
+  g_last_error[0] = 0;
+  if (count < 1 || count > GRINQH_MAX_GROUP)
+    return fail(GRINQH_EINVAL, "count = %d members, expected 1..%d", count, GRINQH_MAX_GROUP);
+  if (!planes || !scales || !zeros || !x || !N || !thresholds || !levels || !n || !y)
+    return fail(GRINQH_EINVAL, "NULL member array");
+  VmmMember mem[GRINQH_MAX_GROUP];
+  for (int m = 0; m < count; ++m) {
+    int st = check_layer(planes[m], scales[m], zeros[m], x[m], y[m], K, N[m], b_max);
+    if (st == GRINQH_OK) st = check_assign_params(thresholds[m], levels[m], n[m], b_max, &mem[m].ap);
+    if (st != GRINQH_OK) {
+      char why[sizeof(g_last_error)];
+      snprintf(why, sizeof(why), "%s", g_last_error);
+      return fail(st, "member %d: %s", m, why);
+    }
+    float* c = clear ? clear[m] : nullptr;
+    if (c) {
+      const uintptr_t c0 = reinterpret_cast<uintptr_t>(c), c1 = c0 + (uintptr_t)N[m] * sizeof(float);
+      for (int k = 0; k < count; ++k) {
+        const uintptr_t y0 = reinterpret_cast<uintptr_t>(y[k]), y1 = y0 + (uintptr_t)N[k] * sizeof(float);
+        if (c0 < y1 && y0 < c1) return fail(GRINQH_EINVAL, "member %d: clear overlaps the y of member %d", m, k);
+      }
+    }
+    mem[m].planes = planes[m];
+    mem[m].scales = scales[m];
+    mem[m].zeros = zeros[m];
+    mem[m].x = x[m];
+    mem[m].y = y[m];
+    mem[m].clear = c;
+    mem[m].N = (int)N[m];
+  }
+  return launch_vmm_group(count, mem, K, b_max, as_stream(stream));
+}
+
 int64_t grinqh_lut_entries(int64_t N, int b_max) {
   if (N <= 0 || b_max < 1 || b_max > GRINQH_MAX_BITS) return -1;
   return N * ((int64_t(1) << (b_max + 1)) - 2);

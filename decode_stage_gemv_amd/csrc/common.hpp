@@ -84,6 +84,28 @@ struct VmmGeometry {
 };
 VmmGeometry vmm_geometry(int64_t K, int64_t N);
 
+// One member of a grouped launch: an independent decode step with its own
+// store, activation, thresholds and output, sharing K and b_max with the
+// other members; `first` is its first workgroup in the grid.
+struct VmmMember {
+  const uint8_t* planes;
+  const uint16_t* scales;
+  const uint16_t* zeros;
+  const uint16_t* x;
+  float* y;
+  float* clear;
+  int N, tiles, first;
+  AssignParams ap;
+};
+
+struct VmmGroup {
+  int count;
+  VmmMember m[GRINQH_MAX_GROUP];
+};
+
+// A grouped accumulating launch (members filled in except tiles and first).
+int launch_vmm_group(int count, VmmMember* members, int64_t K, int bmax, hipStream_t s);
+
 // Launchers (one per .hip file).
 int launch_pack(const uint8_t* codes, int64_t K, int64_t N, int bmax, uint8_t* planes, hipStream_t s);
 int launch_calibrate(const uint16_t* calib, int64_t V, int64_t K, const double* cuts, int n,

@@ -135,6 +135,7 @@ struct VmmArgs {
   int splits, tiles, rows;
   int bmax;   // planes per row of the store (1..8)
   AssignParams ap;
+  VmmGroup group;   // grouped launches only
 };
 
 // First position p in [0, n) with idx[p] >= key (n if none); one full wave.
@@ -277,13 +278,16 @@ enum : int {
 // scalars: the build asks for the first nine arguments to be preloaded into
 // scalar registers, so the activation and scale loads issue at once instead
 // of after a fetch of the argument block, and that fetch (thresholds,
-// levels) completes while the activations are in flight.
-template <bool kFused, int kOut, int kWaves, int kSubs>
-__global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __restrict__ x,
-                                                          const uint8_t* __restrict__ planes,
-                                                          const uint16_t* __restrict__ scales,
-                                                          const uint16_t* __restrict__ zeros, int K, int N,
-                                                          int tiles, int rows, int bmax, VmmArgs a) {
+// levels) completes while the activations are in flight.  kMulti: a grouped
+// launch, where each workgroup first finds its member and takes that
+// member's pointers, shape and thresholds (a few scalar loads).
+template <bool kFused, int kOut, int kWaves, int kSubs, bool kMulti = false>
+__global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __restrict__ x_arg,
+                                                          const uint8_t* __restrict__ planes_arg,
+                                                          const uint16_t* __restrict__ scales_arg,
+                                                          const uint16_t* __restrict__ zeros_arg, int K, int N_arg,
+                                                          int tiles_arg, int rows, int bmax, VmmArgs a) {
+  static_assert(!kMulti || (kFused && kOut == kOutAccumulate), "grouped launches accumulate");
   constexpr int kVmmThreads = 64 * kWaves;
   constexpr int kSubWaves = kWaves / kSubs;         // waves per sub-item
   constexpr int kCols = kTile / kVmmThreads;        // output columns per thread in the epilogue
@@ -301,9 +305,39 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   constexpr bool kParkScales = kSubs > 2;
   __shared__ uint32_t s_scz[kParkScales ? kSubs * kTile : 1];
 
+  const uint16_t* __restrict__ x = x_arg;
+  const uint8_t* __restrict__ planes = planes_arg;
+  const uint16_t* __restrict__ scales = scales_arg;
+  const uint16_t* __restrict__ zeros = zeros_arg;
+  int N = N_arg, tiles = tiles_arg;
+  float* out = a.y;
+  float* clear = a.clear;
+  AssignParams apm;
+  const AssignParams* ap = &a.ap;
+  int bid = blockIdx.x;
+  if constexpr (kMulti) {
+    // the member whose range of workgroups holds this one, then its fields
+    // (an indexed read of the argument block; reading every member's fields
+    // and picking with selects was slower)
+    int m = 0;
+#pragma unroll
+    for (int i = 1; i < GRINQH_MAX_GROUP; ++i) m = (i < a.group.count && bid >= a.group.m[i].first) ? i : m;
+    const VmmMember& mb = a.group.m[m];
+    x = mb.x;
+    planes = mb.planes;
+    scales = mb.scales;
+    zeros = mb.zeros;
+    N = mb.N;
+    tiles = mb.tiles;
+    out = mb.y;
+    clear = mb.clear;
+    apm = mb.ap;
+    ap = &apm;
+    bid -= mb.first;
+  }
   // workgroup = (column tile, item of kSubs sub-items), tiles fastest (K, N < 2^31)
-  const int tile = blockIdx.x % tiles;
-  const int split = blockIdx.x / tiles;
+  const int tile = bid % tiles;
+  const int split = bid / tiles;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -334,7 +368,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   // keep the activation loads ahead of everything else: they need only the
   // preloaded arguments, and waits count loads in issue order
   __builtin_amdgcn_sched_barrier(0);
-  const AssignRegs ar = load_assign_regs(a.ap);   // scalar registers
+  const AssignRegs ar = load_assign_regs(*ap);   // scalar registers
   const int Np = (N + 127) & ~127;
   const int t0 = tile * kTile;
   const int ct = (Np - t0) < kTile ? (Np - t0) : kTile;   // multiple of 128
@@ -611,15 +645,15 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       for (int u = 0; u < kCols; ++u) {
         const int col = tid + u * kVmmThreads;
         if (col < ct && t0 + col < N)
-          __hip_atomic_fetch_add(a.y + t0 + col, val[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(out + t0 + col, val[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     // the caller's next output buffer, zeroed once per column (split 0 only)
-    if (a.clear && split == 0) {
+    if (clear && split == 0) {
 #pragma unroll
       for (int u = 0; u < kCols; ++u) {
         const int col = tid + u * kVmmThreads;
-        if (col < ct && t0 + col < N) a.clear[t0 + col] = 0.0f;
+        if (col < ct && t0 + col < N) clear[t0 + col] = 0.0f;
       }
     }
     return;
@@ -628,7 +662,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
       for (int u = 0; u < kCols; ++u) {
         const int col = tid + u * kVmmThreads;
-        if (col < ct && t0 + col < N) a.y[t0 + col] = val[u];
+        if (col < ct && t0 + col < N) out[t0 + col] = val[u];
       }
       return;
     }
@@ -696,7 +730,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (c4 + e < ct && t0 + c4 + e < N) a.y[t0 + c4 + e] = sum[e];
+        if (c4 + e < ct && t0 + c4 + e < N) out[t0 + c4 + e] = sum[e];
     }
     if (tid == 0) __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -710,8 +744,13 @@ static unsigned* ws_counters(void* ws, int64_t K, int64_t N) {
 }
 
 template <int kWaves, int kSubs>
-static void launch_shape(bool fused, int out_mode, dim3 grid, const VmmArgs& a, hipStream_t s) {
+static void launch_shape(bool fused, int out_mode, dim3 grid, const VmmArgs& a, hipStream_t s, bool multi = false) {
   const dim3 block(64 * kWaves);
+  if (multi) {
+    hipLaunchKernelGGL((vmm_kernel<true, kOutAccumulate, kWaves, kSubs, true>), grid, block, 0, s, a.x, a.planes,
+                       a.scales, a.zeros, (int)a.K, (int)a.N, a.tiles, a.rows, a.bmax, a);
+    return;
+  }
 #define GRINQH_VMM_LAUNCH(F, O)                                                                          \
   hipLaunchKernelGGL((vmm_kernel<F, O, kWaves, kSubs>), grid, block, 0, s, a.x, a.planes, a.scales, a.zeros, \
                      (int)a.K, (int)a.N, a.tiles, a.rows, a.bmax, a)
@@ -729,6 +768,18 @@ static void launch_shape(bool fused, int out_mode, dim3 grid, const VmmArgs& a, 
 #undef GRINQH_VMM_LAUNCH
 }
 
+static bool dispatch_shape(int waves, int subs, bool fused, int out_mode, dim3 grid, const VmmArgs& a,
+                           hipStream_t s, bool multi) {
+  switch (waves * 16 + subs) {
+    case 16 * 16 + 8: launch_shape<16, 8>(fused, out_mode, grid, a, s, multi); return true;
+    case 16 * 16 + 4: launch_shape<16, 4>(fused, out_mode, grid, a, s, multi); return true;
+    case 16 * 16 + 2: launch_shape<16, 2>(fused, out_mode, grid, a, s, multi); return true;
+    case 8 * 16 + 1: launch_shape<8, 1>(fused, out_mode, grid, a, s, multi); return true;
+    case 4 * 16 + 1: launch_shape<4, 1>(fused, out_mode, grid, a, s, multi); return true;
+    default: return false;
+  }
+}
+
 // partials/counters: the split-K workspace (both NULL in accumulate mode).
 static int launch_vmm(bool fused, int out_mode, VmmArgs& a, float* partials, unsigned* counters, hipStream_t s) {
   const VmmGeometry g = vmm_geometry(a.K, a.N);
@@ -743,15 +794,8 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, float* partials, uns
   a.partials = partials;
   a.counters = counters;
   const dim3 grid((unsigned)(g.splits * g.tiles));
-  const int shape = (int)(g.waves * 16 + g.subs);
-  switch (shape) {
-    case 16 * 16 + 8: launch_shape<16, 8>(fused, out_mode, grid, a, s); break;
-    case 16 * 16 + 4: launch_shape<16, 4>(fused, out_mode, grid, a, s); break;
-    case 16 * 16 + 2: launch_shape<16, 2>(fused, out_mode, grid, a, s); break;
-    case 8 * 16 + 1: launch_shape<8, 1>(fused, out_mode, grid, a, s); break;
-    case 4 * 16 + 1: launch_shape<4, 1>(fused, out_mode, grid, a, s); break;
-    default: return fail(GRINQH_EINVAL, "no kernel for %lld waves x %lld sub-items", (long long)g.waves, (long long)g.subs);
-  }
+  if (!dispatch_shape((int)g.waves, (int)g.subs, fused, out_mode, grid, a, s, false))
+    return fail(GRINQH_EINVAL, "no kernel for %lld waves x %lld sub-items", (long long)g.waves, (long long)g.subs);
   return check_launch(out_mode == kOutAccumulate ? "grinqh_decode_vmm_accumulate"
                                                  : (fused ? "grinqh_decode_vmm" : "grinqh_vmm"));
 }
@@ -783,6 +827,42 @@ int launch_vmm_fused_split(const uint8_t* planes, const uint16_t* scales, const 
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.y = y; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
   return launch_vmm(true, kOutSplitK, a, partials, counters, s);
+}
+
+// Several independent accumulating decode steps in one grid: the members'
+// workgroups follow each other (member m from members[m].first), all with
+// the shape chosen for K and the members' column tiles together.
+int launch_vmm_group(int count, VmmMember* members, int64_t K, int bmax, hipStream_t s) {
+  int64_t tiles_total = 0;
+  for (int m = 0; m < count; ++m) tiles_total += n_tiles(members[m].N);
+  const VmmShape sh = choose_shape(K, tiles_total * kTile);
+  const int64_t item = (int64_t)sh.rows * sh.subs;
+  const int64_t splits = (K + item - 1) / item;
+  VmmArgs a{};
+  a.K = K;
+  a.bmax = bmax;
+  a.rows = sh.rows;
+  a.splits = (int)splits;
+  a.group.count = count;
+  int64_t first = 0;
+  for (int m = 0; m < count; ++m) {
+    members[m].tiles = (int)n_tiles(members[m].N);
+    members[m].first = (int)first;
+    first += splits * members[m].tiles;
+    if (first > 0x7FFFFFFF) return fail(GRINQH_EINVAL, "%lld workgroups: more than one launch handles", (long long)first);
+    a.group.m[m] = members[m];
+  }
+  // the preloaded scalar arguments (unused by the grouped kernel): member 0
+  a.x = members[0].x;
+  a.planes = members[0].planes;
+  a.scales = members[0].scales;
+  a.zeros = members[0].zeros;
+  a.N = members[0].N;
+  a.tiles = members[0].tiles;
+  a.y = members[0].y;
+  if (!dispatch_shape(sh.waves, sh.subs, true, kOutAccumulate, dim3((unsigned)first), a, s, true))
+    return fail(GRINQH_EINVAL, "no kernel for %d waves x %d sub-items", sh.waves, sh.subs);
+  return check_launch("grinqh_decode_vmm_accumulate_group");
 }
 
 int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,

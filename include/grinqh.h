@@ -68,6 +68,7 @@ enum {
 #define GRINQH_TILE 1024          /* columns per row tile of the store */
 #define GRINQH_MAX_THRESHOLDS 8   /* n <= 8 thresholds, n + 1 <= 9 levels */
 #define GRINQH_MAX_BITS 8         /* largest b_max */
+#define GRINQH_MAX_GROUP 4        /* members of one grouped launch */
 
 /* Version of the store layout described above (4). */
 int grinqh_layout_version(void);
@@ -195,6 +196,38 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
                                  const uint16_t* x, int64_t K, int64_t N, int b_max,
                                  const float* thresholds, const uint8_t* levels, int n,
                                  float* y, float* clear, void* stream);
+
+/*
+ * Several independent accumulating decode steps in one launch (sections 3.1
+ * and 3.3, each step as grinqh_decode_vmm_accumulate): member m computes
+ *   y[m][j] += (x[m] W[m])[j],  j < N[m],
+ * with its own store, scales, zeros, activation, thresholds and levels.
+ * Meant for the projections of a layer that read the same position of the
+ * model (q, k and v; gate and up), which a decode step can issue together:
+ * one launch instead of count, and the members' column tiles fill the CUs
+ * together.  Each member's result is the one grinqh_decode_vmm_accumulate
+ * gives up to the order of the fp32 additions (the workgroup shape is chosen
+ * for the members together).
+ * count:      1 .. GRINQH_MAX_GROUP members.
+ * planes, scales, zeros, x, y: host arrays of count device pointers, each as
+ *             in grinqh_decode_vmm_accumulate for a K x N[m] layer.
+ * K, b_max:   shared by all members.
+ * N:          host int64 [count].
+ * thresholds, levels: host arrays of count host pointers; n: host int
+ *             [count]; member m's as in grinqh_decode_vmm.
+ * clear:      NULL, or a host array of count pointers each NULL or an fp32
+ *             [N[m]] buffer that this call zeroes; a clear buffer must not
+ *             overlap any member's y.  Members' y may be the same buffer
+ *             (their contributions add).
+ * Errors: EINVAL for count outside 1..GRINQH_MAX_GROUP, NULL arrays, a
+ * clear buffer overlapping a y, and anything grinqh_decode_vmm_accumulate
+ * rejects for a member.
+ */
+int grinqh_decode_vmm_accumulate_group(int count, const uint8_t* const* planes, const uint16_t* const* scales,
+                                       const uint16_t* const* zeros, const uint16_t* const* x, int64_t K,
+                                       const int64_t* N, int b_max, const float* const* thresholds,
+                                       const uint8_t* const* levels, const int* n, float* const* y,
+                                       float* const* clear, void* stream);
 
 /*
  * Look-up-table reconstruction of nested non-uniform weights (section 3.3:

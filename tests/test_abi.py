@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for name in names:
         assert hasattr(lib, name), name
         assert name in g._SIGNATURES, name
@@ -231,7 +231,44 @@ def test_noalloc_validation(lib):
     assert f(p, p, p, p, 256, 256, 9, th, lv, 2, p, None) == g.EINVAL
     lv_hi = (ctypes.c_uint8 * 3)(0, 2, 8)
     assert f(p, p, p, p, 256, 256, 4, th, lv_hi, 2, p, None) == g.EINVAL     # level above b_max
-    # 65536 x 65536: 512 row splits x 65536 fp32 partials = 128 MiB > 16 MiB
+    # 65536 x 65536: 64 row splits x 65536 fp32 partials = 16 MiB, more than
+    # the array holds next to its tile counters
     assert f(p, p, p, p, 65536, 65536, 8, th, lv, 2, p, None) == g.EINVAL
     assert b"allocation-free" in lib.grinqh_last_error()
     assert g.lib().grinqh_workspace_bytes(65536, 65536) > (16 << 20)
+
+
+def test_group_validation(lib):
+    """The grouped entry point checks the member count, its host arrays, each
+    member as the single-layer call would, and clear buffers against every
+    member's output, before any HIP call (pointers are never dereferenced)."""
+    f = lib.grinqh_decode_vmm_accumulate_group
+    P = ctypes.c_void_p
+
+    def arr(*v):
+        return (ctypes.c_void_p * len(v))(*v)
+
+    th = (ctypes.c_float * 2)(0.5, 1.0)
+    lv = (ctypes.c_uint8 * 3)(0, 2, 8)
+    a = 1 << 20
+    planes, sc, zr, xx = arr(a, a), arr(a, a), arr(a, a), arr(a, a)
+    N = (ctypes.c_int64 * 2)(256, 512)
+    ths = arr(ctypes.cast(th, P).value, ctypes.cast(th, P).value)
+    lvs = arr(ctypes.cast(lv, P).value, ctypes.cast(lv, P).value)
+    ns = (ctypes.c_int * 2)(2, 2)
+    y = arr(1 << 24, 2 << 24)
+    assert f(0, planes, sc, zr, xx, 256, N, 8, ths, lvs, ns, y, None, None) == g.EINVAL
+    assert f(5, planes, sc, zr, xx, 256, N, 8, ths, lvs, ns, y, None, None) == g.EINVAL
+    assert f(2, None, sc, zr, xx, 256, N, 8, ths, lvs, ns, y, None, None) == g.EINVAL
+    assert f(2, planes, sc, zr, xx, 256, None, 8, ths, lvs, ns, y, None, None) == g.EINVAL
+    bad_n = (ctypes.c_int64 * 2)(256, 0)
+    assert f(2, planes, sc, zr, xx, 256, bad_n, 8, ths, lvs, ns, y, None, None) == g.EINVAL
+    assert b"member 1" in lib.grinqh_last_error()
+    lv9 = (ctypes.c_uint8 * 3)(0, 2, 9)
+    lvs_bad = arr(ctypes.cast(lv, P).value, ctypes.cast(lv9, P).value)
+    assert f(2, planes, sc, zr, xx, 256, N, 8, ths, lvs_bad, ns, y, None, None) == g.EINVAL
+    assert b"member 1" in lib.grinqh_last_error()
+    # member 0's clear buffer overlapping member 1's y (2 << 24 .. + 2 KiB)
+    clear = arr((2 << 24) + 512, None)
+    assert f(2, planes, sc, zr, xx, 256, N, 8, ths, lvs, ns, y, clear, None) == g.EINVAL
+    assert b"overlaps" in lib.grinqh_last_error()

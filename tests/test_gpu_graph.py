@@ -59,6 +59,8 @@ def test_graph_replays_match_eager_and_oracle():
     X = synthetic.make_activations(512, 130, config=5, matrix=9)
     Xd = _dev(X)
     Yp = torch.empty((130, 384), dtype=torch.float32, device="cuda")
+    # grouped launches: two members on the same store with their own x
+    gy = [torch.zeros(N, dtype=torch.float32, device="cuda") for _ in range(4)]
 
     def steps():
         for k in range(4):   # decode loop: add into one buffer, clear the other
@@ -70,6 +72,10 @@ def test_graph_replays_match_eager_and_oracle():
             grq.decode_vmm_lut(lplanes, lut, lxd, Kl, Nl, lth, levels, lbufs[k % 2],
                                lbufs[(k + 1) % 2])
         grq.prefill(pplanes, psc, pzr, Xd, 512, 384, out=Yp)
+        for half in range(2):   # add into one pair, clear the other
+            a, c = (0, 2) if half == 0 else (2, 0)
+            grq.decode_vmm_accumulate_group([(planes, sc, zr, xs[0], N, th, levels, gy[a], gy[c]),
+                                             (planes, sc, zr, xs[1], N, th, levels, gy[a + 1], gy[c + 1])], K)
 
     lxd = _dev(lx)
     psc, pzr = _dev(play.scales), _dev(play.zeros)
@@ -97,7 +103,7 @@ def test_graph_replays_match_eager_and_oracle():
     pmag = oracle.prefill_abs(play.codes, play.scales, play.zeros, X)
     for rep in range(3):
         # eager work between replays, touching the same buffers
-        for t in (bufs + lbufs + [y_split, y_list, Yp]):
+        for t in (bufs + lbufs + gy + [y_split, y_list, Yp]):
             t.fill_(float(rep + 7))
         grq.decode_vmm(planes, sc, zr, xs[0], K, N, th, levels, ws, out=y_split)
         torch.cuda.synchronize()
@@ -114,4 +120,7 @@ def test_graph_replays_match_eager_and_oracle():
         assert np.all(np.abs(ly - lref) <= REL_TOL * lmag + ABS_TOL)
         assert torch.count_nonzero(lbufs[0]).item() == 0
         assert torch.equal(Yp, eager_prefill)
+        _check(gy[2].cpu().numpy(), lay.codes, lay.scales, lay.zeros, lay.x[0], oracle.assign(lay.x[0], th, levels))
+        _check(gy[3].cpu().numpy(), lay.codes, lay.scales, lay.zeros, lay.x[1], oracle.assign(lay.x[1], th, levels))
+        assert torch.count_nonzero(gy[0]).item() == 0 and torch.count_nonzero(gy[1]).item() == 0
         assert np.all(np.abs(Yp.cpu().numpy().astype(np.float64) - pref) <= REL_TOL * pmag + ABS_TOL)

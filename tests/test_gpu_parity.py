@@ -442,3 +442,33 @@ def test_every_workgroup_shape(K, N, cfg, mat, P, levels):
     torch.cuda.synchronize()
     assert np.array_equal(y2.cpu().numpy().view(np.uint32), y.view(np.uint32))
     _check_y(acc.cpu().numpy(), lay.codes, lay.scales, lay.zeros, x, bits)
+
+
+# ------------------------------------------------------- grouped launches
+
+@pytest.mark.parametrize("K,Ns,b_max", [(4096, (4096, 1024, 1024), 8), (1000, (300, 1100, 70, 2080), 8),
+                                        (4096, (12288, 12288), 8), (777, (1056, 513), 6), (64, (33,), 8)])
+def test_grouped_launch_members(K, Ns, b_max):
+    """Every member of a grouped launch against the oracle on every column,
+    each with its own store, activation and thresholds; the clear buffers
+    zeroed; members that share no shape with the group's choice included."""
+    members, refs = [], []
+    for i, N in enumerate(Ns):
+        lay = synthetic.make_layer(K, N, config=5, matrix=20 + i, n_test=1, b_max=b_max)
+        levels = (0, 2, 3, 4, b_max) if b_max > 4 else (0, 1, 2, 3, 4)
+        th = oracle.calibrate(lay.calib, synthetic.P_LEVELS_5[3])
+        x = lay.x[0]
+        y0 = np.random.default_rng(i).standard_normal(N).astype(np.float32)
+        y = _dev(y0.copy())
+        clear = torch.ones(N, dtype=torch.float32, device="cuda")
+        members.append((grq.pack(_dev(lay.codes), b_max=b_max), _dev(lay.scales), _dev(lay.zeros), _dev(x), N, th,
+                        levels, y, clear))
+        refs.append((lay, x, oracle.assign(x, th, levels), y0))
+    grq.decode_vmm_accumulate_group(members, K, b_max=b_max)
+    torch.cuda.synchronize()
+    for m, (lay, x, bits, y0) in zip(members, refs):
+        assert torch.count_nonzero(m[8]).item() == 0
+        ref = oracle.vmm(lay.codes, lay.scales, lay.zeros, x, bits, b_max=b_max) + y0.astype(np.float64)
+        mag = oracle.vmm_abs(lay.codes, lay.scales, lay.zeros, x, bits, b_max=b_max) + np.abs(y0.astype(np.float64))
+        err = np.abs(m[7].cpu().numpy().astype(np.float64) - ref)
+        assert np.all(err <= REL_TOL * mag + ABS_TOL)

@@ -1,7 +1,8 @@
-"""One token through the 36-layer Qwen3-8B linear stack (252 VMMs, or 144
-with q|k|v and gate|up packed side by side; the whole 8-plane store
-resident), in the launch configuration the stack benchmark times, checked on
-sampled columns of every VMM against the fp64 oracle.
+"""One token through the 36-layer Qwen3-8B linear stack (252 VMMs in 252
+launches or, grouped, in 144; or 144 VMMs with q|k|v and gate|up packed side
+by side; the whole 8-plane store resident), in the launch configuration the
+stack benchmark times, checked on sampled columns of every VMM against the
+fp64 oracle.
 
 Per matrix: the GPU's calibrated thresholds must equal the oracle's bit for
 bit, and every sampled output must satisfy
@@ -24,12 +25,14 @@ REL_TOL = 1e-3
 ABS_TOL = 1e-4
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["per-matrix", "fused-projections"])
-def test_qwen3_stack_one_token_sampled_columns(fused):
+@pytest.mark.parametrize("fused,grouped", [(False, False), (False, True), (True, False)],
+                         ids=["per-matrix", "per-matrix-grouped-launches", "fused-projections"])
+def test_qwen3_stack_one_token_sampled_columns(fused, grouped):
     import bench
-    print(f"building the Qwen3-8B stack (fused={fused})", file=sys.stderr, flush=True)
-    st = bench.Stack(keep_cols=6, fused=fused)
+    print(f"building the Qwen3-8B stack (fused={fused}, grouped={grouped})", file=sys.stderr, flush=True)
+    st = bench.Stack(keep_cols=6, fused=fused, grouped=grouped)
     assert len(st.mats) == (144 if fused else 252)
+    assert st.launches == (252 if not (fused or grouped) else 144)
     st.token(0)                      # adds into output set 0 (zero), clears set 1
     torch.cuda.synchronize()
     bad = []
