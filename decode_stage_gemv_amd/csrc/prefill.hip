@@ -28,9 +28,11 @@
 //      rows; inside each 32-column word the column is XOR-swizzled by the
 //      word index, so writes spread over the banks and fragment reads are
 //      conflict-free.  The step's scale and zero of every column go to LDS.
-//   3. A lane dequantises each B fragment right after reading it: w = s q + z
+//   3. A lane dequantises each B fragment after reading it: w = s q + z
 //      with one packed fp16 fused multiply-add per two weights (one rounding
-//      to fp16, the same weights as the unpacked path).
+//      to fp16, the same weights as the unpacked path).  Within a step the
+//      fragments of the next 16 rows are read while the MFMAs of the current
+//      ones issue.
 //   X, B and the scales are double-buffered in LDS (one barrier per step);
 //   the step after next is loaded into registers meanwhile, and the two
 //   waves sharing a SIMD do the matrix and the unpack halves of a step in
@@ -238,7 +240,43 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[rb][cb][v] = 0.0f;
 
-  // MFMAs of one step from LDS buffer buf
+  // MFMAs of one step from LDS buffer buf.  With 16-byte X loads the
+  // sub-steps are pipelined: while the MFMAs of sub-step s16 issue, the
+  // fragments of s16 + 1 are read from LDS (each A fragment right behind the
+  // two MFMAs that last use the registers it replaces) and its weights are
+  // dequantised afterwards, so the LDS latency hides behind matrix work
+  // instead of stalling every sub-step.  The 2-byte X form holds twice the X
+  // registers and has no room for a second set of fragments: it reads each
+  // sub-step's fragments after the previous sub-step's MFMAs.
+  constexpr bool kPipe = VEC;
+  auto read_b = [&](int buf, int s16, uint32_t (&raw)[2][4]) {
+    const int kb = 2 * s16 + (lane >> 5);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int wi = 2 * wc + cb;                        // 32-column word of the quarter
+      __builtin_memcpy(raw[cb], &s_w[buf][(kb * kPN + 32 * wi + ((lane & 31) ^ wi)) * 4], 16);
+    }
+  };
+  auto read_a = [&](int buf, int s16, int rb, half8_t& af) {
+    const int row = 128 * wr + 32 * rb + (lane & 31);
+    __builtin_memcpy(&af, &s_x[buf][row * kXPitch + 16 * s16 + 8 * (lane >> 5)], 16);
+  };
+  // w = s q + z on both halves of every dword (the raw words are copied
+  // through plain arrays: taking elements of a loaded vector inside a bit
+  // cast made this compiler read only the first dword)
+  auto dequant = [&](const uint32_t (&raw)[2][4], const uint32_t (&s2)[2], const uint32_t (&z2)[2],
+                     half8_t (&bf)[2]) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      uint32_t wv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        wv[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, raw[cb][e]),
+                                                                       __builtin_bit_cast(half2_t, s2[cb]),
+                                                                       __builtin_bit_cast(half2_t, z2[cb])));
+      __builtin_memcpy(&bf[cb], wv, 16);
+    }
+  };
   auto mfma_step = [&](int buf) {
     uint32_t s2[2], z2[2];
 #pragma unroll
@@ -247,38 +285,38 @@ __global__ __launch_bounds__(kPThreads) void prefill_kernel(PrefillArgs a) {
       s2[cb] = (sz & 0xFFFFu) * 0x00010001u;
       z2[cb] = (sz >> 16) * 0x00010001u;
     }
+    half8_t af[4], bf[2];
+    uint32_t raw[2][4];
+    read_b(buf, 0, raw);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) read_a(buf, 0, rb, af[rb]);
+    dequant(raw, s2, z2, bf);
 #pragma unroll
     for (int s16 = 0; s16 < kPK / 16; ++s16) {
-      half8_t af[4], bf[2];
-      const int kb = 2 * s16 + (lane >> 5);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const int wi = 2 * wc + cb;                      // 32-column word of the quarter
-        // copied into plain arrays: taking elements of a loaded vector inside
-        // a bit cast made this compiler read only the first dword
-        uint32_t raw[4], wv[4];
-        __builtin_memcpy(raw, &s_w[buf][(kb * kPN + 32 * wi + ((lane & 31) ^ wi)) * 4], 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          wv[e] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, raw[e]),
-                                                                         __builtin_bit_cast(half2_t, s2[cb]),
-                                                                         __builtin_bit_cast(half2_t, z2[cb])));
-        __builtin_memcpy(&bf[cb], wv, 16);
-      }
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int row = 128 * wr + 32 * rb + (lane & 31);
-        __builtin_memcpy(&af[rb], &s_x[buf][row * kXPitch + 16 * s16 + 8 * (lane >> 5)], 16);
-      }
+      const bool more = s16 + 1 < kPK / 16;
+      if (kPipe && more) read_b(buf, s16 + 1, raw);
+      __builtin_amdgcn_sched_barrier(0);
       // the wave issuing MFMAs goes first while it does (the other wave on
       // the SIMD is loading or unpacking): keeps the matrix core fed
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
+        if (kPipe && more) read_a(buf, s16 + 1, rb, af[rb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       __builtin_amdgcn_s_setprio(0);
+      if (more) {
+        if constexpr (!kPipe) {
+          read_b(buf, s16 + 1, raw);
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) read_a(buf, s16 + 1, rb, af[rb]);
+        }
+        dequant(raw, s2, z2, bf);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
