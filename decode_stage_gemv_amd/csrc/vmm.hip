@@ -534,10 +534,12 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   float acc[32];
 #pragma unroll
   for (int c = 0; c < 32; ++c) acc[c] = 0.0f;
-  // the prologue's own loads (x, scale, zero) have landed long ago; from here
-  // on vmcnt counts only record loads
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  // The scale and zero loads may still be in flight (a cold group's come from
+  // HBM): the record loads issue behind them without waiting, and the
+  // compiler's counts wait for them only where they are used.  Parking them
+  // in LDS uses them here.
   if constexpr (kParkScales) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
     for (int si = 0; si < kSubs; ++si)
 #pragma unroll
