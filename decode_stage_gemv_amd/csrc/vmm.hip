@@ -78,6 +78,11 @@ struct VmmShape {
   int waves, subs, rows;
 };
 
+// Rows of a sub-item of each shape: 64 in the 8-wave single-item shape (small
+// layers), 128 in the others.  A grouped launch's kernel takes it from here
+// rather than from an argument.
+__host__ __device__ constexpr int group_rows(int waves, int subs) { return waves == 8 && subs == 1 ? 64 : 128; }
+
 // Pick the workgroup shape whose busiest CU holds the fewest rows, among
 // shapes whose whole grid is resident at once (at most 16 waves per CU, the
 // kernels' occupancy); ties go to the larger workgroup (one schedule per
@@ -279,8 +284,10 @@ enum : int {
 // scalar registers, so the activation and scale loads issue at once instead
 // of after a fetch of the argument block, and that fetch (thresholds,
 // levels) completes while the activations are in flight.  kMulti: a grouped
-// launch, where each workgroup first finds its member and takes that
-// member's pointers, shape and thresholds (a few scalar loads).
+// launch, where the same leading arguments carry the members' activation
+// pointers and workgroup ranges instead, so a workgroup finds its member and
+// starts its activation loads from registers; the member's other pointers,
+// shape and thresholds follow from the argument block (a few scalar loads).
 template <bool kFused, int kOut, int kWaves, int kSubs, bool kMulti = false>
 __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __restrict__ x_arg,
                                                           const uint8_t* __restrict__ planes_arg,
@@ -293,6 +300,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   constexpr int kCols = kTile / kVmmThreads;        // output columns per thread in the epilogue
   constexpr int kMaxRecords = (kMaxCouples + kSubWaves - 1) / kSubWaves;
   constexpr int kRedWords = kWaves * 32 * kRedStride;
+  constexpr int kGroupRows = group_rows(kWaves, kSubs);   // a grouped launch's sub-item rows
   __shared__ float s_red[kRedWords];                      // wave reduction
   __shared__ uint32_t s_src[kWaves][kMaxRecords * 4];     // per wave: record row -> source byte offset
   __shared__ uint32_t s_cx[kWaves][kMaxRecords * 2];      // per wave: record pair -> fp16 x of its rows
@@ -315,15 +323,25 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   AssignParams apm;
   const AssignParams* ap = &a.ap;
   int bid = blockIdx.x;
+  int tile, split;
   if constexpr (kMulti) {
-    // the member whose range of workgroups holds this one, then its fields
-    // (an indexed read of the argument block; reading every member's fields
-    // and picking with selects was slower)
-    int m = 0;
-#pragma unroll
-    for (int i = 1; i < GRINQH_MAX_GROUP; ++i) m = (i < a.group.count && bid >= a.group.m[i].first) ? i : m;
+    // Grouped launch: the preloaded leading arguments carry every member's
+    // activation pointer (x_arg, planes_arg, scales_arg, zeros_arg: members
+    // 0..3) and the first workgroup of members 1..3 (N_arg, tiles_arg, rows;
+    // past the grid for absent members), so the member and its activations
+    // need no memory access.  Inside a member the workgroups run split
+    // fastest, so its rows do not depend on its tile count; the member's
+    // other fields (scalar loads) arrive while the activations load.
+    const int m = (bid >= N_arg ? 1 : 0) + (bid >= tiles_arg ? 1 : 0) + (bid >= rows ? 1 : 0);
+    bid -= m == 0 ? 0 : (m == 1 ? N_arg : (m == 2 ? tiles_arg : rows));
+    x = m == 0 ? x_arg
+               : (m == 1 ? reinterpret_cast<const uint16_t*>(planes_arg) : (m == 2 ? scales_arg : zeros_arg));
+    rows = kGroupRows;
+    constexpr int kItem = kGroupRows * kSubs;
+    const int splits = (K + kItem - 1) / kItem;
+    split = bid % splits;
+    tile = bid / splits;
     const VmmMember& mb = a.group.m[m];
-    x = mb.x;
     planes = mb.planes;
     scales = mb.scales;
     zeros = mb.zeros;
@@ -333,11 +351,11 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     clear = mb.clear;
     apm = mb.ap;
     ap = &apm;
-    bid -= mb.first;
+  } else {
+    // workgroup = (column tile, item of kSubs sub-items), tiles fastest (K, N < 2^31)
+    tile = bid % tiles;
+    split = bid / tiles;
   }
-  // workgroup = (column tile, item of kSubs sub-items), tiles fastest (K, N < 2^31)
-  const int tile = bid % tiles;
-  const int split = bid / tiles;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -854,13 +872,18 @@ int launch_vmm_group(int count, VmmMember* members, int64_t K, int bmax, hipStre
     if (first > 0x7FFFFFFF) return fail(GRINQH_EINVAL, "%lld workgroups: more than one launch handles", (long long)first);
     a.group.m[m] = members[m];
   }
-  // the preloaded scalar arguments (unused by the grouped kernel): member 0
+  if (sh.rows != group_rows(sh.waves, sh.subs))
+    return fail(GRINQH_EINVAL, "internal: shape %d x %d x %d has no grouped kernel", sh.waves, sh.subs, sh.rows);
+  // the preloaded scalar arguments of a grouped launch: the members'
+  // activation pointers, then the first workgroup of members 1..3 (INT_MAX
+  // for absent members)
   a.x = members[0].x;
-  a.planes = members[0].planes;
-  a.scales = members[0].scales;
-  a.zeros = members[0].zeros;
-  a.N = members[0].N;
-  a.tiles = members[0].tiles;
+  a.planes = reinterpret_cast<const uint8_t*>(members[count > 1 ? 1 : 0].x);
+  a.scales = members[count > 2 ? 2 : 0].x;
+  a.zeros = members[count > 3 ? 3 : 0].x;
+  a.N = count > 1 ? members[1].first : 0x7FFFFFFF;
+  a.tiles = count > 2 ? members[2].first : 0x7FFFFFFF;
+  a.rows = count > 3 ? members[3].first : 0x7FFFFFFF;
   a.y = members[0].y;
   if (!dispatch_shape(sh.waves, sh.subs, true, kOutAccumulate, dim3((unsigned)first), a, s, true))
     return fail(GRINQH_EINVAL, "no kernel for %d waves x %d sub-items", sh.waves, sh.subs);
