@@ -446,8 +446,12 @@ def test_every_workgroup_shape(K, N, cfg, mat, P, levels):
 
 # ------------------------------------------------------- grouped launches
 
+# the group's shape (waves x sub-items x rows) in order: 8x1x64, 8x1x64,
+# 4x1x128, 8x1x64, 8x1x64, 16x2x128, 16x4x128, 16x8x128
 @pytest.mark.parametrize("K,Ns,b_max", [(4096, (4096, 1024, 1024), 8), (1000, (300, 1100, 70, 2080), 8),
-                                        (4096, (12288, 12288), 8), (777, (1056, 513), 6), (64, (33,), 8)])
+                                        (4096, (12288, 12288), 8), (777, (1056, 513), 6), (64, (33,), 8),
+                                        (4096, (8192, 6144), 8), (4096, (16384, 16384), 8),
+                                        (8192, (14336, 14336), 8)])
 def test_grouped_launch_members(K, Ns, b_max):
     """Every member of a grouped launch against the oracle on every column,
     each with its own store, activation and thresholds; the clear buffers
