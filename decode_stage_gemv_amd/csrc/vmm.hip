@@ -17,8 +17,10 @@
 // a bucket is padded with empty rows: x = 0, no bytes).  A couple is two row
 // pairs; the two 32-lane halves of a wave take one pair each, lane l owning
 // 32 columns (one plane word of each row), so the bit width is the same for
-// the whole wave.  Couple k belongs to wave k mod W of the sub-item, W its
-// waves (8, 4 or 2; its "records", in order).
+// the whole wave.  Couple k belongs to the sub-item's wave whose turn is
+// k mod W, W its waves (8, 4 or 2; its "records", in order); the turns start
+// at a different wave in each sub-item of a workgroup, so the waves that get
+// one couple more sit on different SIMDs.
 //
 // Loads.  A lane loads its pair's plane words straight into registers with
 // 4-byte buffer loads: planes p < b come from the row tile; a record is 8
@@ -461,9 +463,18 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
   for (int v = 1; v <= 8; ++v) cbv[v + 1] = cbv[v] + ((cnt[v] + 3) >> 2);
   const int ncp = cbv[9];
-  const int nrec = ncp > swid ? (ncp - swid + kSubWaves - 1) / kSubWaves : 0;   // this wave's couples
+  // couples go to the sub-item's waves in turn from a rotated start, so that
+  // the sub-items' leftover couples (the waves that get one more) fall on
+  // different SIMDs (wave w runs on SIMD w mod 4)
+  constexpr int kSimds = 4;
+  const int first_simd = kSubs == 1 ? 0
+                       : (kSubWaves >= kSimds ? (sub * (kSimds / (kSubs < kSimds ? kSubs : kSimds))) % kSimds
+                                              : ((sub * kSubWaves) % kSimds) + ((sub >> 1) & 1));
+  const int rot = kSubWaves >= kSimds ? first_simd : (first_simd - sub * kSubWaves) & (kSimds - 1);
+  const int cw = (swid + kSubWaves - rot) & (kSubWaves - 1);   // the wave's turn
+  const int nrec = ncp > cw ? (ncp - cw + kSubWaves - 1) / kSubWaves : 0;   // this wave's couples
 
-  if (swid == kSubWaves - 1) {
+  if (cw == kSubWaves - 1) {
     // H = sum x phi and X = sum x over the sub-item's active rows (its last
     // wave has the fewest records, so this stays off the longest path)
     float hs = 0.0f, xs = 0.0f;
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   // padding places, all in vector registers at once
   int rec_w = 0;
   {
-    const int k = swid + kSubWaves * lane;
+    const int k = cw + kSubWaves * lane;
     if (lane < kMaxRecords && k < ncp) {
       int v = 1;
 #pragma unroll
@@ -528,7 +539,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
         }
       }
       const int k = cb + (rank >> 2);
-      if ((k & (kSubWaves - 1)) == swid) {
+      if ((k & (kSubWaves - 1)) == cw) {
         const int j = k / kSubWaves;
         src[4 * j + (rank & 3)] = (uint32_t)rq[e] * (uint32_t)rstride;
         reinterpret_cast<uint16_t*>(cx)[4 * j + (rank & 3)] = xq[e];
