@@ -463,20 +463,20 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
   for (int v = 1; v <= 8; ++v) cbv[v + 1] = cbv[v] + ((cnt[v] + 3) >> 2);
   const int ncp = cbv[9];
-  // couples go to the sub-item's waves in turn from a rotated start, so that
-  // the sub-items' leftover couples (the waves that get one more) fall on
-  // different SIMDs (wave w runs on SIMD w mod 4)
-  constexpr int kSimds = 4;
-  const int first_simd = kSubs == 1 ? 0
-                       : (kSubWaves >= kSimds ? (sub * (kSimds / (kSubs < kSimds ? kSubs : kSimds))) % kSimds
-                                              : ((sub * kSubWaves) % kSimds) + ((sub >> 1) & 1));
-  const int rot = kSubWaves >= kSimds ? first_simd : (first_simd - sub * kSubWaves) & (kSimds - 1);
+  // Couples go to the sub-item's waves in turn.  Wave w runs on SIMD w mod 4,
+  // and the waves that get one couple more are the first turns, so each
+  // sub-item starts its turns on a different SIMD: rot is the wave (within
+  // the sub-item) that takes turn 0.
+  int rot = 0;
+  if constexpr (kSubs == 2) rot = 2 * sub;              // 8 waves each: turn 0 on SIMD 0, 2
+  else if constexpr (kSubs == 4) rot = sub;             // 4 waves each: SIMD 0, 1, 2, 3
+  else if constexpr (kSubs == 8) rot = (sub >> 1) & 1;  // 2 waves each, on SIMDs 2s mod 4 and + 1
   const int cw = (swid + kSubWaves - rot) & (kSubWaves - 1);   // the wave's turn
   const int nrec = ncp > cw ? (ncp - cw + kSubWaves - 1) / kSubWaves : 0;   // this wave's couples
 
   if (cw == kSubWaves - 1) {
-    // H = sum x phi and X = sum x over the sub-item's active rows (its last
-    // wave has the fewest records, so this stays off the longest path)
+    // H = sum x phi and X = sum x over the sub-item's active rows (the last
+    // turn has the fewest records, so this stays off the longest path)
     float hs = 0.0f, xs = 0.0f;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
