@@ -496,13 +496,20 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     }
   }
 
-  // ---- this wave's records: every lane writes the source offset and x of
-  // its own rows that fall into one of them; lanes 0..3 mark padding rows
+  // ---- this wave's records: every slot of the wave's table starts as a
+  // padding row (out-of-range source, x = 0), then every lane writes the
+  // source offset and x of its own rows that fall into one of the records
+  // over it (one wave's LDS writes land in program order)
   uint32_t* const src = s_src[wid];
   uint32_t* const cx = s_cx[wid];
-  // lane j < kMaxRecords describes record j (couple swid + W j): its width
-  // (0 if the wave has no such record) and, for a width's last couple, the
-  // padding places, all in vector registers at once
+#pragma unroll
+  for (int i = 0; i < kMaxRecords * 4; i += 64)
+    if (i + lane < kMaxRecords * 4) src[i + lane] = kOutOfRange;
+#pragma unroll
+  for (int i = 0; i < kMaxRecords * 4; i += 64)   // as halves: the rows' writes below are halves too
+    if (i + lane < kMaxRecords * 4) reinterpret_cast<uint16_t*>(cx)[i + lane] = 0;
+  // lane j < kMaxRecords holds the width of record j (couple cw + W j; 0 if
+  // the wave has no such record)
   int rec_w = 0;
   {
     const int k = cw + kSubWaves * lane;
@@ -510,17 +517,6 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       int v = 1;
 #pragma unroll
       for (int u = 2; u <= 8; ++u) v += k >= cbv[u] ? 1 : 0;
-      int cv = 0, cbs = 0;
-#pragma unroll
-      for (int u = 1; u <= 8; ++u) {
-        cv = u == v ? cnt[u] : cv;
-        cbs = u == v ? cbv[u] : cbs;
-      }
-      const int nreal = cv - 4 * (k - cbs);        // rows present in this couple (>= 1)
-      for (int t = nreal; t < 4; ++t) {
-        src[4 * lane + t] = kOutOfRange;
-        reinterpret_cast<uint16_t*>(cx)[4 * lane + t] = 0;
-      }
       rec_w = v;
     }
   }
