@@ -38,6 +38,8 @@ struct AssignRegs {
   float th[kMaxThresholds];
   int step[kMaxThresholds];
   int lv0;
+  uint32_t lvb[2];   // levels[0..7], one per byte
+  uint32_t lv8;      // levels[8]
 };
 
 __device__ inline AssignRegs load_assign_regs(const AssignParams& ap) {
@@ -48,19 +50,29 @@ __device__ inline AssignRegs load_assign_regs(const AssignParams& ap) {
     r.step[t] = __builtin_amdgcn_readfirstlane((int)ap.lv[t + 1] - (int)ap.lv[t]);
   }
   r.lv0 = __builtin_amdgcn_readfirstlane((int)ap.lv[0]);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    r.lvb[h] = __builtin_amdgcn_readfirstlane(ap.lv[4 * h] | (ap.lv[4 * h + 1] << 8) | (ap.lv[4 * h + 2] << 16) |
+                                              (ap.lv[4 * h + 3] << 24));
+  r.lv8 = __builtin_amdgcn_readfirstlane(ap.lv[kMaxThresholds]);
   return r;
 }
 
-// b = levels[#thresholds reached].  With non-decreasing thresholds the
-// reached ones are a prefix, so b = levels[0] plus the steps of the reached
-// thresholds (a sum, so no table lookup).  Slots past n hold +inf and a zero
-// step (set by the host), so all slots are compared.
+// b = levels[#thresholds reached] (the thresholds do not decrease, so the
+// reached ones are a prefix).  Slots past n hold +inf and repeat levels[n]
+// (set by the host), so all slots are compared without looking at n: a
+// count of compares, then one byte select from the packed level table.
+// (The assignment kernel's width_of adds the level steps of the reached
+// thresholds instead, over the first NT slots only.)
 __device__ inline uint32_t bits_of(uint16_t xh, const AssignRegs& r) {
   const float ax = __builtin_fabsf(half_bits_to_float(xh));
-  int b = r.lv0;
+  uint32_t c = 0;
 #pragma unroll
-  for (int t = 0; t < kMaxThresholds; ++t) b += ax >= r.th[t] ? r.step[t] : 0;
-  return (uint32_t)b;
+  for (int t = 0; t < kMaxThresholds; ++t) c += ax >= r.th[t] ? 1u : 0u;
+  // levels[c]: byte c of the packed table (selectors 0..3 pick the second
+  // operand's bytes, 4..7 the first's), levels[8] past it
+  const uint32_t b = __builtin_amdgcn_perm(r.lvb[1], r.lvb[0], c) & 0xFFu;
+  return c < kMaxThresholds ? b : r.lv8;
 }
 
 // Host-side status plumbing and argument checks (api.hip).
