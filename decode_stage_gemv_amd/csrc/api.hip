@@ -20,6 +20,21 @@ int fail(int status, const char* fmt, ...) {
 
 void clear_error() { g_last_error[0] = 0; }
 
+// [a, a + na) and [b, b + nb) share a byte.
+static bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// A buffer the call zeroes while it reads x and adds into y may overlap
+// neither (its writes land while other workgroups still read x).
+static int check_clear(const float* clear, const float* y, const uint16_t* x, int64_t K, int64_t N) {
+  if (!clear) return GRINQH_OK;
+  if (overlaps(clear, (uint64_t)N * 4, y, (uint64_t)N * 4)) return fail(GRINQH_EINVAL, "clear overlaps y");
+  if (overlaps(clear, (uint64_t)N * 4, x, (uint64_t)K * 2)) return fail(GRINQH_EINVAL, "clear overlaps x");
+  return GRINQH_OK;
+}
+
 int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GRINQH_EDEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -190,12 +205,8 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
                                  float* y, float* clear, void* stream) {
   g_last_error[0] = 0;
   int st = check_layer(planes, scales, zeros, x, y, K, N, b_max);
+  if (st == GRINQH_OK) st = check_clear(clear, y, x, K, N);
   if (st != GRINQH_OK) return st;
-  if (clear) {
-    const uintptr_t c0 = reinterpret_cast<uintptr_t>(clear), y0 = reinterpret_cast<uintptr_t>(y);
-    const uintptr_t len = (uintptr_t)N * sizeof(float);
-    if (c0 < y0 + len && y0 < c0 + len) return fail(GRINQH_EINVAL, "clear overlaps y");
-  }
   AssignParams ap;
   st = check_assign_params(thresholds, levels, n, b_max, &ap);
   if (st != GRINQH_OK) return st;
@@ -223,10 +234,11 @@ int grinqh_decode_vmm_accumulate_group(int count, const uint8_t* const* planes, 
     }
     float* c = clear ? clear[m] : nullptr;
     if (c) {
-      const uintptr_t c0 = reinterpret_cast<uintptr_t>(c), c1 = c0 + (uintptr_t)N[m] * sizeof(float);
       for (int k = 0; k < count; ++k) {
-        const uintptr_t y0 = reinterpret_cast<uintptr_t>(y[k]), y1 = y0 + (uintptr_t)N[k] * sizeof(float);
-        if (c0 < y1 && y0 < c1) return fail(GRINQH_EINVAL, "member %d: clear overlaps the y of member %d", m, k);
+        if (overlaps(c, (uint64_t)N[m] * 4, y[k], (uint64_t)N[k] * 4))
+          return fail(GRINQH_EINVAL, "member %d: clear overlaps the y of member %d", m, k);
+        if (overlaps(c, (uint64_t)N[m] * 4, x[k], (uint64_t)K * 2))
+          return fail(GRINQH_EINVAL, "member %d: clear overlaps the x of member %d", m, k);
       }
     }
     mem[m].planes = planes[m];
@@ -251,12 +263,8 @@ int grinqh_decode_vmm_lut(const uint8_t* planes, const uint16_t* lut, const uint
   g_last_error[0] = 0;
   if (!lut) return fail(GRINQH_EINVAL, "NULL data pointer");
   int st = check_layer(planes, lut, lut, x, y, K, N, b_max);
+  if (st == GRINQH_OK) st = check_clear(clear, y, x, K, N);
   if (st != GRINQH_OK) return st;
-  if (clear) {
-    const uintptr_t c0 = reinterpret_cast<uintptr_t>(clear), y0 = reinterpret_cast<uintptr_t>(y);
-    const uintptr_t len = (uintptr_t)N * sizeof(float);
-    if (c0 < y0 + len && y0 < c0 + len) return fail(GRINQH_EINVAL, "clear overlaps y");
-  }
   AssignParams ap;
   st = check_assign_params(thresholds, levels, n, b_max, &ap);
   if (st != GRINQH_OK) return st;

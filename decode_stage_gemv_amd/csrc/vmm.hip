@@ -410,6 +410,16 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       zr[si][u] = zeros[gs * N + gc];
     }
   }
+  if constexpr (kOut == kOutAccumulate) {
+    // the caller's next output buffer, zeroed once per column (split 0 only)
+    if (clear && split == 0) {
+#pragma unroll
+      for (int u = 0; u < kCols; ++u) {
+        const int col = tid + u * kVmmThreads;
+        if (col < ct && t0 + col < N) clear[t0 + col] = 0.0f;
+      }
+    }
+  }
 
   if constexpr (kFused) {
 #pragma unroll
@@ -673,14 +683,6 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
         const int col = tid + u * kVmmThreads;
         if (col < ct && t0 + col < N)
           __hip_atomic_fetch_add(out + t0 + col, val[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    // the caller's next output buffer, zeroed once per column (split 0 only)
-    if (clear && split == 0) {
-#pragma unroll
-      for (int u = 0; u < kCols; ++u) {
-        const int col = tid + u * kVmmThreads;
-        if (col < ct && t0 + col < N) clear[t0 + col] = 0.0f;
       }
     }
     return;

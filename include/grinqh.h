@@ -188,9 +188,9 @@ int grinqh_decode_vmm(const uint8_t* planes, const uint16_t* scales, const uint1
  *        pass the residual stream of a projection that adds into it.
  * clear: fp32 [N] or NULL.  When given, this call sets it to zero, so a decode
  *        loop can alternate two output buffers without a separate fill launch.
- *        It must not overlap y.
+ *        It must not overlap y or x (it is zeroed while x is still read).
  * Other arguments as in grinqh_decode_vmm (no workspace).
- * Errors: as grinqh_decode_vmm, and EINVAL when clear overlaps y.
+ * Errors: as grinqh_decode_vmm, and EINVAL when clear overlaps y or x.
  */
 int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                                  const uint16_t* x, int64_t K, int64_t N, int b_max,
@@ -217,10 +217,10 @@ int grinqh_decode_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, 
  *             [count]; member m's as in grinqh_decode_vmm.
  * clear:      NULL, or a host array of count pointers each NULL or an fp32
  *             [N[m]] buffer that this call zeroes; a clear buffer must not
- *             overlap any member's y.  Members' y may be the same buffer
- *             (their contributions add).
+ *             overlap any member's y or x.  Members' y may be the same
+ *             buffer (their contributions add).
  * Errors: EINVAL for count outside 1..GRINQH_MAX_GROUP, NULL arrays, a
- * clear buffer overlapping a y, and anything grinqh_decode_vmm_accumulate
+ * clear buffer overlapping a y or an x, and anything grinqh_decode_vmm_accumulate
  * rejects for a member.
  */
 int grinqh_decode_vmm_accumulate_group(int count, const uint8_t* const* planes, const uint16_t* const* scales,
@@ -254,7 +254,7 @@ int64_t grinqh_lut_entries(int64_t N, int b_max);
  * x:       fp16 [K].  thresholds, levels, n: as in grinqh_assign_bits, levels
  *          at most b_max.
  * y:       fp32 [N], read and updated.  clear: fp32 [N] or NULL, set to zero
- *          by this call (it must not overlap y).
+ *          by this call (it must not overlap y or x).
  * Errors: as grinqh_decode_vmm_accumulate, and EINVAL for a NULL or
  * misaligned table.
  */

@@ -128,6 +128,9 @@ def test_accumulate_validation(lib):
     # clear overlapping y is rejected; clear == NULL is allowed (fails later only on bad args)
     r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, 1, y, y + 128, None)
     assert r == g.EINVAL and "overlap" in _err(lib)
+    # so is clear overlapping x (K = 128 halves from FAKE): it is zeroed while x is read
+    r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, 1, y, FAKE + 200, None)
+    assert r == g.EINVAL and "overlaps x" in _err(lib)
     r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, 1, None, None, None)
     assert r == g.EINVAL
     r = lib.grinqh_decode_vmm_accumulate(FAKE, FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, -2, y, None, None)
@@ -198,6 +201,8 @@ def test_lut_validation(lib):
     assert r == g.EINVAL
     r = lib.grinqh_decode_vmm_lut(FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, 1, y, y + 64, None)
     assert r == g.EINVAL and "overlap" in _err(lib)
+    r = lib.grinqh_decode_vmm_lut(FAKE, FAKE, FAKE, 128, 64, 8, thp, lvp, 1, y, FAKE - 16, None)
+    assert r == g.EINVAL and "overlaps x" in _err(lib)
     r = lib.grinqh_decode_vmm_lut(FAKE, FAKE + 2, FAKE, 128, 64, 8, thp, lvp, 1, y, None, None)
     assert r == g.EINVAL and "aligned" in _err(lib)
     r = lib.grinqh_decode_vmm_lut(FAKE, FAKE, FAKE, 128, 64, 4, thp, lvp, 1, y, None, None)
@@ -272,3 +277,7 @@ def test_group_validation(lib):
     clear = arr((2 << 24) + 512, None)
     assert f(2, planes, sc, zr, xx, 256, N, 8, ths, lvs, ns, y, clear, None) == g.EINVAL
     assert b"overlaps" in lib.grinqh_last_error()
+    # member 1's clear buffer overlapping the members' x (1 << 20 .. + 512 bytes)
+    clear = arr(None, a + 256)
+    assert f(2, planes, sc, zr, xx, 256, N, 8, ths, lvs, ns, y, clear, None) == g.EINVAL
+    assert b"clear overlaps the x" in lib.grinqh_last_error()
