@@ -678,6 +678,72 @@ def linear_fit(points):
     return {"intercept_us": float(a), "bw_eff_GB_s": float(1e-3 / slope) if slope > 0 else None, "r2": r2}
 
 
+TIMELINE_PHASES = {
+    "accumulate": [(0, "start"), (1, "widths known"), (2, "buckets counted"), (3, "record tables written"),
+                   (4, "first three records issued"), (5, "waves reduced"), (6, "atomics issued"),
+                   (7, "atomics acknowledged")],
+    "decode": [(0, "start"), (1, "widths known"), (2, "buckets counted"), (3, "record tables written"),
+               (4, "first three records issued"), (5, "waves reduced"), (6, "partial row acknowledged"),
+               (7, "tile sum written (last workgroup of a tile)")],
+}
+
+
+def _timeline_summary(stamps, mask, phases):
+    """Percentiles (0, 10, 50, 90, 100) over the launch's workgroups of each
+    stamp, in microseconds after the first workgroup started (100 MHz clock)."""
+    import decode_stage_gemv_amd as grq
+    st = stamps.reshape(grq.TIMELINE_WORKGROUPS, grq.TIMELINE_SLOTS)[mask].astype(np.int64)
+    t0 = st[:, 0].min()
+
+    def pct(v):
+        return [round(float(np.percentile(v, q)), 2) for q in (0, 10, 50, 90, 100)]
+
+    out = {}
+    for slot, label in phases:
+        col = st[:, slot]
+        valid = col >= t0      # a slot a workgroup did not record this launch holds an older value
+        if valid.any():
+            out[label] = pct((col[valid] - t0) / 100.0)
+    waves = st[:, 8:8 + 16]
+    ok = waves >= t0
+    if ok.any():
+        first = np.where(ok, waves, np.iinfo(np.int64).max).min(axis=1)
+        last = np.where(ok, waves, np.iinfo(np.int64).min).max(axis=1)
+        out["records done (first wave)"] = pct((first - t0) / 100.0)
+        out["records done (last wave)"] = pct((last - t0) / 100.0)
+    return out
+
+
+def timeline_bench(name, mode, steps, warmup):
+    """Where a launch's time goes, from the timeline build's clock stamps: one
+    launch after host-launched warm-up steps, and the last step of a HIP-graph
+    replay of `steps` steps (each step on a different rotated copy, as in the
+    timed runs)."""
+    import torch
+    import decode_stage_gemv_amd as grq
+    prep = Prepared(name, mode)
+    for k in range(max(warmup, 2 * prep.R)):
+        prep.step(k)
+    torch.cuda.synchronize()
+    s1 = grq.timeline_read()
+    prep.step(0)
+    torch.cuda.synchronize()
+    s2 = grq.timeline_read()
+    # the launch's workgroups are the ones whose start stamp changed
+    mask = s2.reshape(-1, grq.TIMELINE_SLOTS)[:, 0] != s1.reshape(-1, grq.TIMELINE_SLOTS)[:, 0]
+    res = {"workload": name, "entry_point": ENTRY[mode], "workgroups": int(mask.sum()),
+           "units": "us after the first workgroup started; percentiles 0/10/50/90/100 over workgroups",
+           "host_launch": _timeline_summary(s2, mask, TIMELINE_PHASES[mode])}
+    ms, _ = prep.run(steps, 0, graph=True)
+    s3 = grq.timeline_read()
+    res["graph_replay"] = _timeline_summary(s3, mask, TIMELINE_PHASES[mode])
+    res["graph_replay_us_per_step"] = ms * 1e3
+    for form in ("host_launch", "graph_replay"):
+        for label, v in res[form].items():
+            log(f"timeline {name} {form}: {label:40s} {v}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -707,6 +773,9 @@ def main():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the Qwen3-8B stack leg (252 VMMs per token, 6.95 GB of planes)")
     ap.add_argument("--stack-only", action="store_true", help="time only the Qwen3-8B stack")
+    ap.add_argument("--timeline", action="store_true",
+                    help="load the timeline build (libgrinqh_timeline.so, `python -m decode_stage_gemv_amd.build "
+                         "--timeline`) and report where a launch of the chosen workload and mode spends its time")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this decode VMM path runs on a single GPU "
@@ -717,6 +786,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.timeline:
+        import decode_stage_gemv_amd as grq
+        grq.use_library(grq.TIMELINE_LIB_PATH)
+        scrub_init()
+        mode = args.mode if args.mode in TIMELINE_PHASES else "accumulate"
+        print(json.dumps({"timeline": timeline_bench(args.workload, mode, min(args.steps, 100),
+                                                     args.warmup)}), flush=True)
+        return
     scrub_init()
     if args.copy_probe:
         print(json.dumps({"copy_probe": copy_probe()}), flush=True)

@@ -10,7 +10,7 @@ call raises.
 Names follow the C ABI in ``include/grinqh.h``:
 ``pack``, ``calibrate``, ``assign_bits``, ``vmm``, ``decode_vmm``,
 ``decode_vmm_noalloc``, ``decode_vmm_accumulate``, ``decode_vmm_lut``, ``prefill``, ``unpack_dense``,
-``dense_gemm``.
+``dense_gemm``, and ``timeline_read`` (measurement aid of the timeline build).
 """
 from __future__ import annotations
 
@@ -67,7 +67,21 @@ _SIGNATURES = {
     "grinqh_dense_gemm": ([_vp, _vp, _i64, _i64, _i64, _vp, _vp], _i32),
     "grinqh_decode_vmm_noalloc": ([_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp], _i32),
     "grinqh_decode_vmm_lut": ([_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _vp], _i32),
+    "grinqh_timeline_read": ([_vp, _i64], _i32),
 }
+
+TIMELINE_LIB_PATH = os.path.join(HERE, "libgrinqh_timeline.so")
+TIMELINE_WORKGROUPS = 8192
+TIMELINE_SLOTS = 24
+
+
+def use_library(path: str) -> None:
+    """Load the library from `path` instead of ``libgrinqh.so`` (before the
+    first call; bench.py uses it for the timeline build, TIMELINE_LIB_PATH)."""
+    global LIB_PATH
+    if _lib is not None and os.path.abspath(path) != os.path.abspath(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is already loaded")
+    LIB_PATH = os.path.abspath(path)
 
 
 def lib() -> ctypes.CDLL:
@@ -380,4 +394,14 @@ def dense_gemm(X, dense, K: int, N: int, out=None, stream=None):
     _dev(out, "Y", torch.float32, (M, N))
     _check("grinqh_dense_gemm", lib().grinqh_dense_gemm(X.data_ptr(), dense.data_ptr(), M, K, N, out.data_ptr(),
                                                         _stream(stream)))
+    return out
+
+
+def timeline_read(count: int = TIMELINE_WORKGROUPS * TIMELINE_SLOTS):
+    """The timeline build's clock stamps (see grinqh_timeline_read): a numpy
+    uint64 array of `count` stamps, workgroup-major, TIMELINE_SLOTS per
+    workgroup.  Raises GrinqhError (ENOSYS) with the ordinary library."""
+    import numpy as np
+    out = np.zeros(count, dtype=np.uint64)
+    _check("grinqh_timeline_read", lib().grinqh_timeline_read(out.ctypes.data, count))
     return out

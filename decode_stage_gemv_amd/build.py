@@ -1,6 +1,9 @@
 """Build libgrinqh.so (all HIP sources, gfx950) in place next to this file.
 
-Usage: python -m decode_stage_gemv_amd.build
+Usage: python -m decode_stage_gemv_amd.build [--timeline]
+
+--timeline builds libgrinqh_timeline.so instead: the same library with the
+VMM's clock stamps compiled in (grinqh_timeline_read), for measurement only.
 """
 from __future__ import annotations
 
@@ -13,6 +16,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libgrinqh.so")
+# the same sources with the VMM's clock stamps compiled in (a measurement aid;
+# see grinqh_timeline_read in include/grinqh.h)
+LIB_TIMELINE = os.path.join(HERE, "libgrinqh_timeline.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -55,17 +61,19 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Compile libgrinqh.so (or, with timeline=True, libgrinqh_timeline.so)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *sources(), "-o", tmp]
+    out = LIB_TIMELINE if timeline else LIB
+    tmp = out + ".tmp"
+    cmd = [hipcc, *FLAGS, *(["-DGRINQH_TIMELINE"] if timeline else []), "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(HERE, "csrc"), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libgrinqh.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
     usage = resource_usage(res.stderr)
     if not usage:
         raise RuntimeError("no kernel resource report from hipcc")
@@ -80,9 +88,9 @@ def build(verbose: bool = False) -> str:
     if verbose:
         for name, u in sorted(usage.items()):
             print(f"  {name}: {u}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))

@@ -74,8 +74,9 @@ __host__ __device__ inline void planes_to_codes(const uint32_t (&w)[8], uint32_t
   uint32_t v[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) v[r] = (7 - r < B) ? w[7 - r] : 0u;
-  if constexpr (B <= 2) {
-    // few planes: plain shifts and masks, which the compiler folds well
+  if constexpr (B <= 1) {
+    // one plane: plain shifts and masks, which the compiler folds well (from
+    // two planes on, the zero-aware stages below take fewer instructions)
 #pragma unroll
     for (int r = 0; r < 4; ++r) swap_blocks<4, 0x0F0F0F0Fu>(v[r], v[r + 4]);
 #pragma unroll

@@ -40,6 +40,7 @@ struct AssignRegs {
   int lv0;
   uint32_t lvb[2];   // levels[0..7], one per byte
   uint32_t lv8;      // levels[8]
+  int n;             // thresholds in use
 };
 
 __device__ inline AssignRegs load_assign_regs(const AssignParams& ap) {
@@ -55,22 +56,44 @@ __device__ inline AssignRegs load_assign_regs(const AssignParams& ap) {
     r.lvb[h] = __builtin_amdgcn_readfirstlane(ap.lv[4 * h] | (ap.lv[4 * h + 1] << 8) | (ap.lv[4 * h + 2] << 16) |
                                               (ap.lv[4 * h + 3] << 24));
   r.lv8 = __builtin_amdgcn_readfirstlane(ap.lv[kMaxThresholds]);
+  r.n = __builtin_amdgcn_readfirstlane(ap.n);
   return r;
 }
 
-// b = levels[#thresholds reached] (the thresholds do not decrease, so the
-// reached ones are a prefix).  Slots past n hold +inf and repeat levels[n]
-// (set by the host), so all slots are compared without looking at n: a
-// count of compares, then one byte select from the packed level table.
-// (The assignment kernel's width_of adds the level steps of the reached
-// thresholds instead, over the first NT slots only.)
+// b = levels[#thresholds reached] for two rows at once (the thresholds do
+// not decrease, so the reached ones are a prefix).  Only the n thresholds in
+// use are compared, behind a wave-uniform test: past them every slot holds
+// +inf, which only |x| = +inf reaches, and levels[c] = levels[n] for every
+// such count c anyway.  The level is one byte select from the packed level
+// table.  (The assignment kernel's width_of adds the level steps of the
+// reached thresholds instead, over the first NT slots only.)
+__device__ inline void bits_of2(uint16_t xh0, uint16_t xh1, const AssignRegs& r, uint32_t& b0, uint32_t& b1) {
+  const float a0 = __builtin_fabsf(half_bits_to_float(xh0));
+  const float a1 = __builtin_fabsf(half_bits_to_float(xh1));
+  uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+  for (int t = 0; t < kMaxThresholds; ++t) {
+    if (t < r.n) {   // wave-uniform
+      c0 += a0 >= r.th[t] ? 1u : 0u;
+      c1 += a1 >= r.th[t] ? 1u : 0u;
+    }
+  }
+  // levels[c]: byte c of the packed table (selectors 0..3 pick the second
+  // operand's bytes, 4..7 the first's), levels[8] past it
+  const uint32_t l0 = __builtin_amdgcn_perm(r.lvb[1], r.lvb[0], c0) & 0xFFu;
+  const uint32_t l1 = __builtin_amdgcn_perm(r.lvb[1], r.lvb[0], c1) & 0xFFu;
+  b0 = c0 < kMaxThresholds ? l0 : r.lv8;
+  b1 = c1 < kMaxThresholds ? l1 : r.lv8;
+}
+
+// The same for one row.
 __device__ inline uint32_t bits_of(uint16_t xh, const AssignRegs& r) {
   const float ax = __builtin_fabsf(half_bits_to_float(xh));
   uint32_t c = 0;
 #pragma unroll
-  for (int t = 0; t < kMaxThresholds; ++t) c += ax >= r.th[t] ? 1u : 0u;
-  // levels[c]: byte c of the packed table (selectors 0..3 pick the second
-  // operand's bytes, 4..7 the first's), levels[8] past it
+  for (int t = 0; t < kMaxThresholds; ++t) {
+    if (t < r.n) c += ax >= r.th[t] ? 1u : 0u;   // wave-uniform test
+  }
   const uint32_t b = __builtin_amdgcn_perm(r.lvb[1], r.lvb[0], c) & 0xFFu;
   return c < kMaxThresholds ? b : r.lv8;
 }

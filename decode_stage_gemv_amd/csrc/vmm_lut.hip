@@ -449,7 +449,8 @@ void vmm_lut_kernel(const uint16_t* __restrict__ xp, const uint16_t* __restrict_
     const int64_t n = n0 + tid;
     if (n < N) {
       if (nrows > 0) __hip_atomic_fetch_add(a.y + n, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (a.clear && split == 0) a.clear[n] = 0.0f;
+      // device scope: written through, no dirty line left for the kernel's end
+      if (a.clear && split == 0) __hip_atomic_store(a.clear + n, 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -60,8 +60,8 @@ enum {
     GRINQH_OK = 0,
     GRINQH_EINVAL = -1,   /* bad argument; nothing was enqueued */
     GRINQH_EDEVICE = -2,  /* HIP reported an error (no device, launch failure) */
-    GRINQH_ENOSYS = -3    /* reserved for an entry point without an implementation;
-                             every call declared here is implemented, so none returns it */
+    GRINQH_ENOSYS = -3    /* the library was built without the feature the call needs
+                             (only grinqh_timeline_read, outside a timeline build) */
 };
 
 #define GRINQH_GROUP 128          /* rows per (scale, zero) group */
@@ -332,6 +332,32 @@ int grinqh_dense_gemm(const uint16_t* X, const void* dense, int64_t M, int64_t K
 int grinqh_decode_vmm_noalloc(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                               const uint16_t* x, int64_t K, int64_t N, int b_max,
                               const float* thresholds, const uint8_t* levels, int n, float* y, void* stream);
+
+/*
+ * Measurement aid, not part of the decode path.  A library built with
+ * GRINQH_TIMELINE defined (libgrinqh_timeline.so, `python -m
+ * decode_stage_gemv_amd.build --timeline`) records, in every plain
+ * (not grouped) VMM launch, the GPU's 100 MHz constant clock at fixed points
+ * of each workgroup's work into a device array of
+ * GRINQH_TIMELINE_WORKGROUPS x GRINQH_TIMELINE_SLOTS 64-bit stamps
+ * (workgroup-major; workgroups past the first GRINQH_TIMELINE_WORKGROUPS
+ * record nothing).  Slots, taken by the workgroup's first wave unless noted:
+ *   0 start; 1 widths known (activations arrived); 2 buckets counted;
+ *   3 record tables written; 4 first three records' loads issued;
+ *   5 waves reduced (after the workgroup barrier); 6 atomics issued
+ *   (accumulate) or partial row stored and acknowledged (split-K);
+ *   7 atomics acknowledged (accumulate) or the tile's sum written (split-K,
+ *   the tile's last workgroup only); 8 + w: wave w's records done.
+ * Each launch overwrites the slots it records; other slots keep older values.
+ * grinqh_timeline_read copies the first `count` stamps to host memory
+ * `stamps` (synchronous: it waits for the device).
+ * Errors: ENOSYS in a library built without the timeline; EINVAL for a NULL
+ * buffer or a count outside [0, GRINQH_TIMELINE_WORKGROUPS x
+ * GRINQH_TIMELINE_SLOTS]; EDEVICE if the copy fails.
+ */
+#define GRINQH_TIMELINE_WORKGROUPS 8192
+#define GRINQH_TIMELINE_SLOTS 24
+int grinqh_timeline_read(uint64_t* stamps, int64_t count);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for name in names:
         assert hasattr(lib, name), name
         assert name in g._SIGNATURES, name
@@ -281,3 +281,29 @@ def test_group_validation(lib):
     clear = arr(None, a + 256)
     assert f(2, planes, sc, zr, xx, 256, N, 8, ths, lvs, ns, y, clear, None) == g.EINVAL
     assert b"clear overlaps the x" in lib.grinqh_last_error()
+
+
+def test_timeline_reader_needs_the_timeline_build(lib):
+    """The ordinary library has no clock stamps: the reader says so (ENOSYS)
+    without touching the device."""
+    buf = (ctypes.c_uint64 * 4)()
+    assert lib.grinqh_timeline_read(ctypes.addressof(buf), 4) == g.ENOSYS
+    assert "without the timeline" in _err(lib)
+
+
+def test_timeline_build_exports_the_same_symbols_and_checks_arguments():
+    """The timeline build exports every declared call too, and its reader
+    rejects bad arguments on the host (a zero count copies nothing)."""
+    if not os.path.exists(g.TIMELINE_LIB_PATH):
+        pytest.fail("libgrinqh_timeline.so is not built (python -m decode_stage_gemv_amd.build --timeline)")
+    tl = ctypes.CDLL(g.TIMELINE_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(tl, name), name
+    tl.grinqh_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    tl.grinqh_timeline_read.restype = ctypes.c_int
+    tl.grinqh_last_error.restype = ctypes.c_char_p
+    buf = (ctypes.c_uint64 * 4)()
+    assert tl.grinqh_timeline_read(None, 4) == g.EINVAL
+    assert tl.grinqh_timeline_read(ctypes.addressof(buf), -1) == g.EINVAL
+    assert tl.grinqh_timeline_read(ctypes.addressof(buf), g.TIMELINE_WORKGROUPS * g.TIMELINE_SLOTS + 1) == g.EINVAL
+    assert tl.grinqh_timeline_read(ctypes.addressof(buf), 0) == g.OK
