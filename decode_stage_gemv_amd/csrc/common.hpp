@@ -115,6 +115,7 @@ struct VmmGeometry {
   int64_t tiles;           // column tiles
   int64_t partial_floats;  // splits * N_pad when splits > 1, else 0
   int64_t counter_offset;  // byte offset of the per-tile counters
+  int64_t words_offset;    // byte offset of the column words (2 N_pad of 8 bytes)
   int64_t bytes;           // total workspace bytes
 };
 VmmGeometry vmm_geometry(int64_t K, int64_t N);
@@ -158,8 +159,10 @@ int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16
 // (the allocation-free entry point keeps them in a fixed device array).
 int launch_vmm_fused_split(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                            const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
-                           float* y, float* partials, unsigned* counters, hipStream_t s);
-int noalloc_scratch(int64_t partial_bytes, int64_t tiles, float** partials, unsigned** counters);
+                           float* y, float* partials, unsigned* counters, unsigned long long* words,
+                           int64_t max_cols, hipStream_t s);
+int noalloc_scratch(int64_t partial_bytes, int64_t tiles, int64_t cols, float** partials, unsigned** counters,
+                    unsigned long long** words, int64_t* max_cols);
 int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                           const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
                           float* y, float* clear, hipStream_t s);

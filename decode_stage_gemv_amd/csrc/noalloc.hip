@@ -13,17 +13,21 @@
 
 namespace grinqh {
 
-// Layout of the array: the tile counters at a fixed place at the front (so
-// that every layer shape finds its counters where every earlier call, of any
-// shape, left zeros), the split-K partial rows after them.
+// Layout of the array: the tile counters and the column words (accumulators,
+// then masks) at fixed places at the front, so that every layer shape finds
+// them where every earlier call, of any shape, left zeros; the split-K
+// partial rows after them.
 constexpr size_t kScratchBytes = GRINQH_NOALLOC_SCRATCH_BYTES;
 constexpr size_t kCounterBytes = 64 * 1024;   // up to 16384 column tiles
-constexpr size_t kPartialBytes = kScratchBytes - kCounterBytes;
+constexpr int64_t kMaxWordCols = 262144;      // column words for N up to 262144
+constexpr size_t kWordBytes = 2 * kMaxWordCols * 8;
+constexpr size_t kPartialBytes = kScratchBytes - kCounterBytes - kWordBytes;
 
-// Zero-initialised when the code object is loaded.  The counters must be
-// zero when a call starts: a completed call leaves every counter it used at
-// zero again (the last workgroup of a tile resets it), and the partial rows
-// are always written before they are read.
+// Zero-initialised when the code object is loaded.  The counters and column
+// words must be zero when a call starts: a completed call leaves every
+// counter and word it used at zero again (the last workgroup of a tile, or
+// the last add to a column, resets it), and the partial rows are always
+// written before they are read.
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
@@ -53,7 +57,8 @@ static int scratch_address(void** out) {
   return GRINQH_OK;
 }
 
-int noalloc_scratch(int64_t partial_bytes, int64_t tiles, float** partials, unsigned** counters) {
+int noalloc_scratch(int64_t partial_bytes, int64_t tiles, int64_t cols, float** partials, unsigned** counters,
+                    unsigned long long** words, int64_t* max_cols) {
   if (partial_bytes > (int64_t)kPartialBytes)
     return fail(GRINQH_EINVAL,
                 "layer needs %lld bytes of split-K partials; the allocation-free entry point holds %zu",
@@ -61,11 +66,16 @@ int noalloc_scratch(int64_t partial_bytes, int64_t tiles, float** partials, unsi
   if (tiles * 4 > (int64_t)kCounterBytes)
     return fail(GRINQH_EINVAL, "%lld column tiles; the allocation-free entry point holds %zu",
                 (long long)tiles, kCounterBytes / 4);
+  if (cols > kMaxWordCols)
+    return fail(GRINQH_EINVAL, "%lld padded columns; the allocation-free entry point holds %lld",
+                (long long)cols, (long long)kMaxWordCols);
   void* base = nullptr;
   const int st = scratch_address(&base);
   if (st != GRINQH_OK) return st;
   *counters = reinterpret_cast<unsigned*>(base);
-  *partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(base) + kCounterBytes);
+  *words = reinterpret_cast<unsigned long long*>(reinterpret_cast<uint8_t*>(base) + kCounterBytes);
+  *max_cols = kMaxWordCols;
+  *partials = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(base) + kCounterBytes + kWordBytes);
   return GRINQH_OK;
 }
 
@@ -86,8 +96,10 @@ extern "C" int grinqh_decode_vmm_noalloc(const uint8_t* planes, const uint16_t* 
   const VmmGeometry g = vmm_geometry(K, N);
   float* partials = nullptr;
   unsigned* counters = nullptr;
-  st = noalloc_scratch(g.partial_floats * 4, g.tiles, &partials, &counters);
+  unsigned long long* words = nullptr;
+  int64_t max_cols = 0;
+  st = noalloc_scratch(g.partial_floats * 4, g.tiles, padded_cols(N), &partials, &counters, &words, &max_cols);
   if (st != GRINQH_OK) return st;
-  return launch_vmm_fused_split(planes, scales, zeros, x, K, N, b_max, ap, y, partials, counters,
+  return launch_vmm_fused_split(planes, scales, zeros, x, K, N, b_max, ap, y, partials, counters, words, max_cols,
                                 reinterpret_cast<hipStream_t>(stream));
 }

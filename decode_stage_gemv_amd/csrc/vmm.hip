@@ -72,6 +72,15 @@ constexpr int kScopeDevice = 16;                 // cache-policy bits: sc1 = dev
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14],
 // expcnt [6:4], lgkmcnt [11:8]; all-ones fields mean "do not wait".
 constexpr int kWaitVm0 = 0x0F70;                 // vmcnt(0) only
+// Fixed-point split-K reduction: at most 127 splits (7-bit arrival count),
+// partials below 2^22 in magnitude go as integers in units of 2^-20 (their
+// rounding, at most 2^-21 each, is the only difference from an exact sum),
+// offset by 2^42 so that every added value lies in [0, 2^43]: 127 of them
+// stay below 2^50, the top of the value field.
+constexpr int kFixedMaxSplits = 127;
+constexpr int kFixedFrac = 20;
+constexpr int kFixedOffsetBit = 42;
+constexpr float kFixedLimit = 4194304.0f;        // 2^22
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -145,7 +154,8 @@ VmmGeometry vmm_geometry(int64_t K, int64_t N) {
   g.splits = (K + item - 1) / item;
   g.partial_floats = g.splits > 1 ? g.splits * padded_cols(N) : 0;
   g.counter_offset = (g.partial_floats * 4 + 255) / 256 * 256;
-  g.bytes = g.splits > 1 ? g.counter_offset + g.tiles * 4 : 0;
+  g.words_offset = (g.counter_offset + g.tiles * 4 + 255) / 256 * 256;
+  g.bytes = g.splits > 1 ? g.words_offset + 2 * padded_cols(N) * 8 : 0;
   return g;
 }
 
@@ -161,6 +171,8 @@ struct VmmArgs {
   float* clear;
   float* partials;
   unsigned* counters;
+  unsigned long long* acc_words;    // split-K, up to kFixedMaxSplits: one word per column
+  unsigned long long* mask_words;   // ... and one mask of the splits that sent a float partial
   int64_t K, N;
   int splits, tiles, rows;
   int bmax;   // planes per row of the store (1..8)
@@ -766,6 +778,68 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       }
       return;
     }
+    if (a.splits <= kFixedMaxSplits) {
+      // ---- exact, order-free accumulation (up to kFixedMaxSplits splits).
+      // Every workgroup adds its partial sum p of a column, as the integer
+      // round(p 2^kFixedFrac) offset by 2^kFixedOffsetBit, into the column's
+      // 64-bit word with one device-scope atomic that also counts its
+      // arrival (bits 57..63) and returns the old word.  Integer addition
+      // does not depend on the order of the adds, so the total does not
+      // depend on scheduling, and the thread whose add completes the count
+      // turns the total into y and clears the word for the next call: one
+      // round trip.  A partial too large for the fixed-point range, or not
+      // finite, goes instead as a float to its slot of the partial rows
+      // (acknowledged), then as the split's bit in the column's mask word
+      // (acknowledged), and its add carries only the arrival and a count of
+      // such partials (bits 50..56); the last thread then adds those floats
+      // to the converted total in split order.  Each word holds at most
+      // kFixedMaxSplits offset values of at most 2^(kFixedOffsetBit + 1), so
+      // the value field (bits 0..49) never carries into the counts.
+#pragma unroll
+      for (int u = 0; u < kCols; ++u) {
+        const int col = tid + u * kVmmThreads;
+        if (col >= ct) continue;
+        const int64_t j = t0 + col;
+        const float pv = val[u];
+        unsigned long long add = 1ull << 57;
+        if (__builtin_fabsf(pv) < kFixedLimit) {
+          const float sc = pv * __builtin_bit_cast(float, (uint32_t)(127 + kFixedFrac) << 23);   // exact
+          add += (unsigned long long)((long long)__builtin_rintf(sc) + (1ll << kFixedOffsetBit));
+        } else {
+          __hip_atomic_store(a.partials + (int64_t)split * Np + j, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_amdgcn_s_waitcnt(0);
+          const unsigned long long prev =
+              __hip_atomic_fetch_or(a.mask_words + j, 1ull << split, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          asm volatile("" ::"v"(prev));   // the OR has returned before the add below
+          add += 1ull << 50;
+        }
+        const unsigned long long old =
+            __hip_atomic_fetch_add(a.acc_words + j, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((int)(old >> 57) == a.splits - 1) {
+          const unsigned long long tot = old + add;
+          const int nfloat = (int)((tot >> 50) & 127u);
+          const long long vsum = (long long)(tot & ((1ull << 50) - 1)) -
+                                 (long long)(a.splits - nfloat) * (1ll << kFixedOffsetBit);
+          float yv = (float)((double)vsum * __builtin_bit_cast(double, (uint64_t)(1023 - kFixedFrac) << 52));
+          if (nfloat > 0) {
+            const unsigned long long m = __hip_atomic_load(a.mask_words + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int sp = 0; sp < a.splits; ++sp)
+              if ((m >> sp) & 1ull)
+                yv += __hip_atomic_load(a.partials + (int64_t)sp * Np + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.mask_words + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          __hip_atomic_store(a.acc_words + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (j < N) __hip_atomic_store(out + j, yv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#ifdef GRINQH_TIMELINE
+      __builtin_amdgcn_s_waitcnt(0);
+      GRINQH_STAMP(6, tid == 0);   // timeline: column words added (and, where last, y written)
+#endif
+      return;
+    }
+    // ---- more splits: partial rows, and the last workgroup of the tile adds
+    // them in split order
 #pragma unroll
     for (int u = 0; u < kCols; ++u) {
       const int col = tid + u * kVmmThreads;
@@ -866,8 +940,14 @@ extern "C" int grinqh_timeline_read(uint64_t* stamps, int64_t count) {
 
 namespace grinqh {
 
-// The caller's workspace: partial rows first, the per-tile counters after them.
+// The caller's workspace: partial rows first, the per-tile counters after
+// them, then the column words (one accumulator and one mask per padded column).
 static float* ws_partials(void* ws) { return reinterpret_cast<float*>(ws); }
+static unsigned long long* ws_words(void* ws, int64_t K, int64_t N) {
+  const VmmGeometry g = vmm_geometry(K, N);
+  return g.bytes > 0 && ws ? reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(ws) + g.words_offset)
+                           : nullptr;
+}
 static unsigned* ws_counters(void* ws, int64_t K, int64_t N) {
   const VmmGeometry g = vmm_geometry(K, N);
   return g.bytes > 0 && ws ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(ws) + g.counter_offset) : nullptr;
@@ -911,7 +991,9 @@ static bool dispatch_shape(int waves, int subs, bool fused, int out_mode, dim3 g
 }
 
 // partials/counters: the split-K workspace (both NULL in accumulate mode).
-static int launch_vmm(bool fused, int out_mode, VmmArgs& a, float* partials, unsigned* counters, hipStream_t s) {
+// words: the column accumulators, then (max_cols entries on) the column masks.
+static int launch_vmm(bool fused, int out_mode, VmmArgs& a, float* partials, unsigned* counters,
+                      unsigned long long* words, int64_t max_cols, hipStream_t s) {
   const VmmGeometry g = vmm_geometry(a.K, a.N);
   if (g.splits * g.tiles > 0x7FFFFFFF)
     return fail(GRINQH_EINVAL, "%lld workgroups: more than one launch handles", (long long)(g.splits * g.tiles));
@@ -923,6 +1005,8 @@ static int launch_vmm(bool fused, int out_mode, VmmArgs& a, float* partials, uns
   a.rows = (int)g.rows_per_split;
   a.partials = partials;
   a.counters = counters;
+  a.acc_words = words;
+  a.mask_words = words ? words + max_cols : nullptr;
   const dim3 grid((unsigned)(g.splits * g.tiles));
   if (!dispatch_shape((int)g.waves, (int)g.subs, fused, out_mode, grid, a, s, false))
     return fail(GRINQH_EINVAL, "no kernel for %lld waves x %lld sub-items", (long long)g.waves, (long long)g.subs);
@@ -938,7 +1022,7 @@ int launch_vmm_list(const uint8_t* planes, const uint16_t* scales, const uint16_
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.bits = bits; a.active_idx = active_idx; a.n_active = n_active;
   a.y = y; a.K = K; a.N = N; a.bmax = bmax;
-  return launch_vmm(false, kOutSplitK, a, ws_partials(ws), ws_counters(ws, K, N), s);
+  return launch_vmm(false, kOutSplitK, a, ws_partials(ws), ws_counters(ws, K, N), ws_words(ws, K, N), padded_cols(N), s);
 }
 
 int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
@@ -947,16 +1031,17 @@ int launch_vmm_fused(const uint8_t* planes, const uint16_t* scales, const uint16
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.y = y; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
-  return launch_vmm(true, kOutSplitK, a, ws_partials(ws), ws_counters(ws, K, N), s);
+  return launch_vmm(true, kOutSplitK, a, ws_partials(ws), ws_counters(ws, K, N), ws_words(ws, K, N), padded_cols(N), s);
 }
 
 int launch_vmm_fused_split(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,
                            const uint16_t* x, int64_t K, int64_t N, int bmax, const AssignParams& ap,
-                           float* y, float* partials, unsigned* counters, hipStream_t s) {
+                           float* y, float* partials, unsigned* counters, unsigned long long* words,
+                           int64_t max_cols, hipStream_t s) {
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.y = y; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
-  return launch_vmm(true, kOutSplitK, a, partials, counters, s);
+  return launch_vmm(true, kOutSplitK, a, partials, counters, words, max_cols, s);
 }
 
 // Several independent accumulating decode steps in one grid: the members'
@@ -1006,7 +1091,7 @@ int launch_vmm_accumulate(const uint8_t* planes, const uint16_t* scales, const u
   VmmArgs a{};
   a.planes = planes; a.scales = scales; a.zeros = zeros; a.x = x;
   a.y = y; a.clear = clear; a.K = K; a.N = N; a.bmax = bmax; a.ap = ap;
-  return launch_vmm(true, kOutAccumulate, a, nullptr, nullptr, s);
+  return launch_vmm(true, kOutAccumulate, a, nullptr, nullptr, nullptr, 0, s);
 }
 
 }  // namespace grinqh

@@ -85,13 +85,14 @@ const char* grinqh_last_error(void);
 int64_t grinqh_planes_bytes(int64_t K, int64_t N, int b_max);
 
 /* Workspace bytes grinqh_vmm / grinqh_decode_vmm need for a K x N layer
- * (split-K partial sums and per-tile counters).  Returns -1 for K, N <= 0. */
+ * (split-K partial sums, per-tile counters and two 8-byte words per padded
+ * column).  Returns -1 for K, N <= 0. */
 int64_t grinqh_workspace_bytes(int64_t K, int64_t N);
 
 /* Zero a workspace so it can be used by grinqh_vmm / grinqh_decode_vmm.
  * Needed once after allocation: every successful VMM call leaves the
- * counters at zero again.  Uses a fill kernel, so it may be captured in a
- * HIP graph. */
+ * counters and column words at zero again.  Uses a fill kernel, so it may be
+ * captured in a HIP graph. */
 int grinqh_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -157,6 +158,11 @@ int grinqh_assign_bits(const uint16_t* x, int64_t K, const float* thresholds, co
  * y:          fp32 [N] out (written completely).
  * workspace:  grinqh_workspace_bytes(K, N) bytes, zeroed once with
  *             grinqh_workspace_init.
+ * The K-splits' partial sums are combined so that y does not depend on
+ * scheduling (bit-identical from call to call): up to 127 splits as exact
+ * integer sums of the partials in units of 2^-20 (partials of magnitude 2^22
+ * or more, or not finite, added as floats in split order), beyond that as
+ * floats in split order.
  * Errors: EINVAL for NULL pointers, K, N <= 0, K >= 2^31, b_max outside
  * 1..8, or a workspace smaller than grinqh_workspace_bytes(K, N).
  */
@@ -323,10 +329,9 @@ int grinqh_dense_gemm(const uint16_t* X, const void* dense, int64_t M, int64_t K
  * race and must not be issued; calls in stream order are fine.
  * Arguments, result (bit-identical to grinqh_decode_vmm) and errors as in
  * grinqh_decode_vmm, plus EINVAL when the layer needs more than the array
- * holds (more than GRINQH_NOALLOC_SCRATCH_BYTES - 64 KiB of partial rows, or
- * more than 16384 column tiles; every layer up to 8192 x 28672 and
- * 28672 x 8192 fits) and EDEVICE when the array's device address cannot be
- * obtained.
+ * holds (more than GRINQH_NOALLOC_SCRATCH_BYTES - 4 MiB - 64 KiB of partial
+ * rows, or N above 262144; every layer up to 8192 x 28672 and 28672 x 8192
+ * fits) and EDEVICE when the array's device address cannot be obtained.
  */
 #define GRINQH_NOALLOC_SCRATCH_BYTES (16u << 20)
 int grinqh_decode_vmm_noalloc(const uint8_t* planes, const uint16_t* scales, const uint16_t* zeros,

@@ -312,6 +312,51 @@ def test_deterministic_repeat():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
+def test_split_reduction_large_partials():
+    """The split-K reduction with partial sums on both sides of its
+    fixed-point range (2^22): column j's scale and zero are multiplied by
+    2^(j mod 16) and the activations by 64, so most partials go as integers
+    and some (224 of the 64 x 1024 partials of 64-row splits, counted in
+    fp64 when the test was written) as floats, in one launch.  Within
+    tolerance of the oracle, bit-identical on repeat."""
+    K, N = 4096, 1024
+    lay = layer(K, N, 2, 1)
+    mult = (2.0 ** (np.arange(N) % 16)).astype(np.float32)
+    scales = (lay.scales.astype(np.float32) * mult).astype(np.float16)
+    zeros = (lay.zeros.astype(np.float32) * mult).astype(np.float16)
+    assert np.all(np.isfinite(scales)) and np.all(np.isfinite(zeros))
+    x = (lay.x[0].astype(np.float32) * 64).astype(np.float16)
+    assert np.all(np.isfinite(x))
+    th = oracle.calibrate(lay.calib, synthetic.P_LEVELS_5[3])
+    planes = grq.pack(_dev(lay.codes))
+    ws = grq.make_workspace(K, N)
+    args = (planes, _dev(scales), _dev(zeros), _dev(x), K, N, th, synthetic.LEVELS_5, ws)
+    y1 = grq.decode_vmm(*args).cpu().numpy()
+    y2 = grq.decode_vmm(*args).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    bits = oracle.assign(x, th, synthetic.LEVELS_5)
+    ref = oracle.vmm(lay.codes, scales, zeros, x, bits)
+    assert np.max(np.abs(ref)) > 2.0 ** 24, "no column reaches the float path"
+    _check_y(y1, lay.codes, scales, zeros, x, bits)
+
+
+def test_split_reduction_many_splits():
+    """A tall, narrow layer whose split count (256 splits of 64 rows) is past
+    the fixed-point reduction's 127: the partial-row path, within tolerance
+    and bit-identical on repeat."""
+    K, N = 16384, 256
+    lay = layer(K, N, 5, 5)
+    th = oracle.calibrate(lay.calib, synthetic.P_LEVELS_5[3])
+    planes = grq.pack(_dev(lay.codes))
+    ws = grq.make_workspace(K, N)
+    args = (planes, _dev(lay.scales), _dev(lay.zeros), _dev(lay.x[0]), K, N, th, synthetic.LEVELS_5, ws)
+    y1 = grq.decode_vmm(*args).cpu().numpy()
+    y2 = grq.decode_vmm(*args).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    bits = oracle.assign(lay.x[0], th, synthetic.LEVELS_5)
+    _check_y(y1, lay.codes, lay.scales, lay.zeros, lay.x[0], bits)
+
+
 # ------------------------------------------------- full sizes, every output
 
 FULL = [
