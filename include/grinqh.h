@@ -350,9 +350,11 @@ int grinqh_decode_vmm_noalloc(const uint8_t* planes, const uint16_t* scales, con
  *   0 start; 1 widths known (activations arrived); 2 buckets counted;
  *   3 record tables written; 4 first three records' loads issued;
  *   5 waves reduced (after the workgroup barrier); 6 atomics issued
- *   (accumulate) or partial row stored and acknowledged (split-K);
- *   7 atomics acknowledged (accumulate) or the tile's sum written (split-K,
- *   the tile's last workgroup only); 8 + w: wave w's records done.
+ *   (accumulate), the column words added and acknowledged (split-K up to
+ *   127 splits) or the partial row stored and acknowledged (more splits);
+ *   7 atomics acknowledged (accumulate) or the tile's sum written (split-K
+ *   past 127 splits, the tile's last workgroup only); 8 + w: wave w's
+ *   records done.
  * Each launch overwrites the slots it records; other slots keep older values.
  * grinqh_timeline_read copies the first `count` stamps to host memory
  * `stamps` (synchronous: it waits for the device).
