@@ -11,7 +11,8 @@
 // idle, 4-wave workgroups of one 128-row sub-item share the CUs, and small
 // layers use 8-wave workgroups of one 64-row sub-item (choose_shape).
 //
-// Row order.  Every wave sees all rows of its sub-item (two per lane) and
+// Row order.  Every wave sees all rows of its sub-item (two per lane, one in
+// the 64-row sub-items of the small-layer shape) and
 // buckets the active ones by bit width b with ballots, in registers.  Each
 // bucket is cut into "couples" of four rows of one width (the last couple of
 // a bucket is padded with empty rows: x = 0, no bytes).  A couple is two row
@@ -54,7 +55,6 @@
 namespace grinqh {
 
 constexpr int kMaxRows = kGroup;                 // rows of one workgroup: 128 or 64, within one scale group
-constexpr int kMaxCouples = kMaxRows / 4 + 6;    // sum over 8 widths of ceil(c_v / 4) <= (128 + 8 * 3) / 4
 constexpr int kRedStride = 33;                   // LDS row stride of the wave reduction
 // Launch shape.  The grid is (item, column tile) pairs; an item is S
 // sub-items of R rows (R = 128, or 64 on small layers).  The shapes are
@@ -355,7 +355,8 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   constexpr int kVmmThreads = 64 * kWaves;
   constexpr int kSubWaves = kWaves / kSubs;         // waves per sub-item
   constexpr int kCols = kTile / kVmmThreads;        // output columns per thread in the epilogue
-  constexpr int kMaxRecords = (kMaxCouples + kSubWaves - 1) / kSubWaves;
+  // couples of a sub-item: at most rows / 4 + 6 (sum over 8 widths of ceil(c_v / 4))
+  constexpr int kMaxRecords = (group_rows(kWaves, kSubs) / 4 + 6 + kSubWaves - 1) / kSubWaves;
   constexpr int kRedWords = kWaves * 32 * kRedStride;
   constexpr int kGroupRows = group_rows(kWaves, kSubs);   // a grouped launch's sub-item rows
   __shared__ float s_red[kRedWords];                      // wave reduction
@@ -430,12 +431,15 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   // + 64): activation loads first, then scale and zero of this thread's two
   // output columns (tid, tid + 512).  Loads are unconditional (clamped
   // index, validity applied later) so nothing waits on them early.
-  uint32_t bq[2] = {0u, 0u};   // bit width of the lane's two rows
+  // rows per lane: two for 128-row sub-items, one for 64-row ones (whose
+  // second set would always be empty: no loads, compares or ballots for it)
+  constexpr int kRPL = group_rows(kWaves, kSubs) / 64;
+  uint32_t bq[2] = {0u, 0u};   // bit width of the lane's rows
   uint16_t xq[2] = {0, 0};     // their fp16 activations
   int rq[2] = {0, 0};          // their rows within the group
   if constexpr (kFused) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < kRPL; ++e) {
       const int64_t i = k0 + lane + 64 * e;
       xq[e] = x[i < k1 ? i : (k1 > k0 ? k1 - 1 : K - 1)];
       rq[e] = lane + 64 * e;
@@ -484,10 +488,13 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
   if constexpr (kFused) {
     // both rows' activations were loaded from clamped indexes: widths of
     // rows past the sub-item are dropped afterwards
-    uint32_t b0, b1;
-    bits_of2(xq[0], xq[1], ar, b0, b1);
+    uint32_t b0, b1 = 0;
+    if constexpr (kRPL == 2)
+      bits_of2(xq[0], xq[1], ar, b0, b1);
+    else
+      b0 = bits_of(xq[0], ar);
     bq[0] = k0 + rq[0] < k1 ? b0 : 0u;
-    bq[1] = k0 + rq[1] < k1 ? b1 : 0u;
+    bq[1] = kRPL == 2 && k0 + rq[1] < k1 ? b1 : 0u;
 #ifdef GRINQH_TIMELINE
     asm volatile("" ::"v"(bq[0]), "v"(bq[1]));
 #endif
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     int m = s_p[sub][1] - p0;
     m = m < 0 ? 0 : (m > kMaxRows ? kMaxRows : m);
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < kRPL; ++e) {
       const int q = lane + 64 * e;
       if (q < m) {
         const int64_t i = a.active_idx[p0 + q];
@@ -531,7 +538,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
 #pragma unroll
   for (int v = 1; v <= 8; ++v) {
     msk[0][v] = __ballot(bq[0] == (uint32_t)v);
-    msk[1][v] = __ballot(bq[1] == (uint32_t)v);
+    msk[1][v] = kRPL == 2 ? __ballot(bq[1] == (uint32_t)v) : 0ull;
     cnt[v] = __popcll(msk[0][v]) + __popcll(msk[1][v]);
   }
   int cbv[10];   // first couple of each width; cbv[9] = number of couples
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     // turn has the fewest records, so this stays off the longest path)
     float hs = 0.0f, xs = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < kRPL; ++e) {
       const float xf = bq[e] > 0 ? half_bits_to_float(xq[e]) : 0.0f;
       hs += phi_x((int)bq[e], bmax, xf);
       xs += xf;
@@ -599,7 +606,7 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
     }
   }
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
+  for (int e = 0; e < kRPL; ++e) {
     const uint32_t b = bq[e];
     if (b > 0) {
       int rank = 0, cb = 0;
