@@ -181,9 +181,25 @@ struct VmmArgs {
 };
 
 // First position p in [0, n) with idx[p] >= key (n if none); one full wave.
-__device__ int64_t wave_lower_bound(const int32_t* __restrict__ idx, int64_t n, int64_t key) {
+// The first probe reads the 64 entries around `hint` (where the key would
+// sit if the listed rows were spread evenly over [0, K)): for a list of that
+// kind it nearly always brackets the key, one round trip instead of two or
+// three; otherwise it still narrows the range and the search goes on.
+__device__ int64_t wave_lower_bound(const int32_t* __restrict__ idx, int64_t n, int64_t key, int64_t hint) {
   const int lane = threadIdx.x & 63;
   int64_t lo = 0, hi = n;
+  if (n > 64) {
+    int64_t base = hint - 32;
+    base = base < 0 ? 0 : (base > n - 64 ? n - 64 : base);
+    const uint64_t m = __ballot(idx[base + lane] >= key);
+    if (m == 0) {
+      lo = base + 64;   // every probed entry is below the key
+    } else if (m & 1ull) {
+      hi = base;        // the first probed entry already reaches it: p <= base
+    } else {
+      return base + (__ffsll((unsigned long long)m) - 1);
+    }
+  }
   while (hi > lo) {
     const int64_t span = hi - lo;
     if (span <= 64) {
@@ -508,7 +524,8 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       // the searches stay inside the K entries the list buffer must hold
       int64_t n = *a.n_active;
       n = n < 0 ? 0 : (n > a.K ? a.K : n);
-      const int64_t p = wave_lower_bound(a.active_idx, n, swid == 0 ? k0 : k1);
+      const int64_t key = swid == 0 ? k0 : k1;
+      const int64_t p = wave_lower_bound(a.active_idx, n, key, key * n / a.K);
       if (lane == 0) s_p[sub][swid] = (int)p;
     }
     __syncthreads();
