@@ -241,6 +241,10 @@ def test_noalloc_validation(lib):
     assert f(p, p, p, p, 65536, 65536, 8, th, lv, 2, p, None) == g.EINVAL
     assert b"allocation-free" in lib.grinqh_last_error()
     assert g.lib().grinqh_workspace_bytes(65536, 65536) > (16 << 20)
+    # 2048 x 300032: few partial bytes (two splits) but more columns than the
+    # array's column words cover (262144)
+    assert f(p, p, p, p, 2048, 300032, 8, th, lv, 2, p, None) == g.EINVAL
+    assert b"padded columns" in lib.grinqh_last_error()
 
 
 def test_group_validation(lib):
