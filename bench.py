@@ -689,8 +689,8 @@ TIMELINE_PHASES = {
                    (7, "atomics acknowledged")],
     "decode": [(0, "start"), (1, "widths known"), (2, "buckets counted"), (3, "record tables written"),
                (4, "first three records issued"), (5, "waves reduced"),
-               (6, "column words added, y written where last (up to 127 splits); partial row acknowledged (more)"),
-               (7, "tile sum written (last workgroup of a tile; more than 127 splits)")],
+               (6, "column words added, y written where last (up to 64 splits); partial row acknowledged (more)"),
+               (7, "tile sum written (last workgroup of a tile; more than 64 splits)")],
 }
 
 

@@ -72,12 +72,13 @@ constexpr int kScopeDevice = 16;                 // cache-policy bits: sc1 = dev
 // s_waitcnt immediates (gfx9 encoding): vmcnt in bits [3:0] and [15:14],
 // expcnt [6:4], lgkmcnt [11:8]; all-ones fields mean "do not wait".
 constexpr int kWaitVm0 = 0x0F70;                 // vmcnt(0) only
-// Fixed-point split-K reduction: at most 127 splits (7-bit arrival count),
-// partials below 2^22 in magnitude go as integers in units of 2^-20 (their
-// rounding, at most 2^-21 each, is the only difference from an exact sum),
-// offset by 2^42 so that every added value lies in [0, 2^43]: 127 of them
-// stay below 2^50, the top of the value field.
-constexpr int kFixedMaxSplits = 127;
+// Fixed-point split-K reduction: at most 64 splits (one bit each in the
+// 64-bit mask of float partials; the arrival count takes 7 bits), partials
+// below 2^22 in magnitude go as integers in units of 2^-20 (their rounding,
+// at most 2^-21 each, is the only difference from an exact sum), offset by
+// 2^42 so that every added value lies in [0, 2^43]: 64 of them stay below
+// 2^50, the top of the value field.
+constexpr int kFixedMaxSplits = 64;
 constexpr int kFixedFrac = 20;
 constexpr int kFixedOffsetBit = 42;
 constexpr float kFixedLimit = 4194304.0f;        // 2^22
@@ -818,7 +819,8 @@ __global__ __launch_bounds__(64 * kWaves) void vmm_kernel(const uint16_t* __rest
       // such partials (bits 50..56); the last thread then adds those floats
       // to the converted total in split order.  Each word holds at most
       // kFixedMaxSplits offset values of at most 2^(kFixedOffsetBit + 1), so
-      // the value field (bits 0..49) never carries into the counts.
+      // the value field (bits 0..49) never carries into the counts, and the
+      // split's mask bit (1 << split) stays inside the 64-bit mask.
 #pragma unroll
       for (int u = 0; u < kCols; ++u) {
         const int col = tid + u * kVmmThreads;

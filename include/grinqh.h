@@ -159,7 +159,7 @@ int grinqh_assign_bits(const uint16_t* x, int64_t K, const float* thresholds, co
  * workspace:  grinqh_workspace_bytes(K, N) bytes, zeroed once with
  *             grinqh_workspace_init.
  * The K-splits' partial sums are combined so that y does not depend on
- * scheduling (bit-identical from call to call): up to 127 splits as exact
+ * scheduling (bit-identical from call to call): up to 64 splits as exact
  * integer sums of the partials in units of 2^-20 (partials of magnitude 2^22
  * or more, or not finite, added as floats in split order), beyond that as
  * floats in split order.
@@ -351,9 +351,9 @@ int grinqh_decode_vmm_noalloc(const uint8_t* planes, const uint16_t* scales, con
  *   3 record tables written; 4 first three records' loads issued;
  *   5 waves reduced (after the workgroup barrier); 6 atomics issued
  *   (accumulate), the column words added and acknowledged (split-K up to
- *   127 splits) or the partial row stored and acknowledged (more splits);
+ *   64 splits) or the partial row stored and acknowledged (more splits);
  *   7 atomics acknowledged (accumulate) or the tile's sum written (split-K
- *   past 127 splits, the tile's last workgroup only); 8 + w: wave w's
+ *   past 64 splits, the tile's last workgroup only); 8 + w: wave w's
  *   records done.
  * Each launch overwrites the slots it records; other slots keep older values.
  * grinqh_timeline_read copies the first `count` stamps to host memory
