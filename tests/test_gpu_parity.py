@@ -312,14 +312,16 @@ def test_deterministic_repeat():
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
 
 
-def test_split_reduction_large_partials():
+@pytest.mark.parametrize("K,N", [(4096, 1024), (6144, 256)])
+def test_split_reduction_large_partials(K, N):
     """The split-K reduction with partial sums on both sides of its
     fixed-point range (2^22): column j's scale and zero are multiplied by
-    2^(j mod 16) and the activations by 64, so most partials go as integers
-    and some (224 of the 64 x 1024 partials of 64-row splits, counted in
-    fp64 when the test was written) as floats, in one launch.  Within
-    tolerance of the oracle, bit-identical on repeat."""
-    K, N = 4096, 1024
+    2^(j mod 16) and the activations by 64, so at 4096 x 1024 (64 splits of
+    64 rows, the most the fixed-point words take) most partials go as
+    integers and some (224 of the 64 x 1024, counted in fp64 when the test
+    was written) as floats, in one launch; 6144 x 256 (96 splits) takes the
+    partial rows with the same large values.  Within tolerance of the
+    oracle, bit-identical on repeat."""
     lay = layer(K, N, 2, 1)
     mult = (2.0 ** (np.arange(N) % 16)).astype(np.float32)
     scales = (lay.scales.astype(np.float32) * mult).astype(np.float16)
